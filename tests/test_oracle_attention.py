@@ -1,0 +1,205 @@
+"""Pins of the RoPE, bf16 and attention oracle against closed forms, textbook
+special cases and library routines (never against a retyped copy of itself)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+from oracle import attention as A
+from oracle import selection as S
+from oracle.bf16 import round_bf16
+from oracle.rope import rope
+
+
+# ------------------------------------------------------------------ bf16
+def test_round_bf16_ties_to_even_worked_values():
+    ulp = 2.0 ** -7                       # bf16 spacing in [1, 2)
+    assert round_bf16(1.0 + ulp / 2) == 1.0          # tie -> even (1.0)
+    assert round_bf16(1.0 + 1.5 * ulp) == 1.0 + 2 * ulp   # tie -> even
+    assert round_bf16(1.0 + 0.51 * ulp) == 1.0 + ulp
+    assert round_bf16(-3.0) == -3.0
+    assert round_bf16(0.0) == 0.0
+
+
+def test_round_bf16_matches_torch_on_float32_values():
+    x = np.random.default_rng(0).standard_normal(200000).astype(np.float32) * 37.0
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(round_bf16(x.astype(np.float64)), want)
+
+
+# ------------------------------------------------------------------ RoPE
+def test_rope_position_zero_is_identity_and_norm_preserved():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 3, 64))
+    np.testing.assert_array_equal(rope(x, np.zeros(5), 500000.0), x)
+    y = rope(x, rng.integers(0, 600000, 5), 500000.0)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-12)
+
+
+def test_rope_equals_complex_rotation():
+    """Pair (x_i, x_{i+d/2}) as the complex number x_i + j x_{i+d/2}, multiplied
+    by exp(j * pos * base^(-2i/d))."""
+    rng = np.random.default_rng(2)
+    d, base = 16, 10000.0
+    x = rng.standard_normal((7, 2, d))
+    pos = rng.integers(0, 5000, 7)
+    z = x[..., : d // 2] + 1j * x[..., d // 2:]
+    freqs = np.array([base ** (-2.0 * i / d) for i in range(d // 2)])
+    z = z * np.exp(1j * pos[:, None, None] * freqs[None, None, :])
+    want = np.concatenate([z.real, z.imag], axis=-1)
+    np.testing.assert_allclose(rope(x, pos, base), want, rtol=1e-12, atol=1e-12)
+
+
+def test_rope_scores_depend_only_on_offset():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 1, 128))
+    k = rng.standard_normal((1, 1, 128))
+    base = 500000.0
+    s1 = (rope(q, [1000], base) * rope(k, [400], base)).sum()
+    s2 = (rope(q, [600600], base) * rope(k, [600000], base)).sum()
+    assert s1 == pytest.approx(s2, rel=1e-9, abs=1e-9)
+
+
+# ------------------------------------------------------------ attention
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _bf(x):
+    return round_bf16(x)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (4, 4), (8, 2)])
+def test_single_block_phase1_is_plain_causal_attention(hq, hkv):
+    """With one block there is no prefix: Phase 1 is ordinary causal attention.
+    Checked against torch's scaled_dot_product_attention (float64, causal,
+    grouped-query heads)."""
+    b, d, base = 48, 32, 500000.0
+    q, k, v = _bf(_rand((b, hq, d), 1)), _bf(_rand((b, hkv, d), 2)), _bf(_rand((b, hkv, d), 3))
+    pos = np.arange(b)
+    k_hat = A.rotate_bf16(k, pos, base)
+    got = A.phase1_rows(q, k_hat, v, [np.zeros(0, np.int64)], [(0, r) for r in range(b)], b, base)
+    qh = torch.from_numpy(A.rotate_bf16(q, pos, base)).permute(1, 0, 2)[None]
+    kh = torch.from_numpy(k_hat).permute(1, 0, 2)[None]
+    vh = torch.from_numpy(v).permute(1, 0, 2)[None]
+    want = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, is_causal=True,
+                                                            enable_gqa=(hq != hkv))
+    np.testing.assert_allclose(got, want[0].permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_gather_form_equals_dense_form_with_multiplicity_bias():
+    N, b, chunk, sink, hq, hkv, d, base = 3, 64, 16, 32, 4, 2, 16, 500000.0
+    L = N * b
+    q, k, v = _bf(_rand((L, hq, d), 4)), _bf(_rand((L, hkv, d), 5)), _bf(_rand((L, hkv, d), 6))
+    sel = np.array([[0, 2], [1, 3], [0, 1]])     # chunk 0 of block 0 lies inside the sink
+    pre = S.prefix_positions(sel, N, b, chunk, sink)
+    k_hat = A.rotate_bf16(k, np.arange(L), base)
+    for i in range(N):
+        dense = A.phase1_block_dense(q, k_hat, v, pre[i], i, b, base)
+        rows = A.phase1_rows(q, k_hat, v, pre, [(i, r) for r in range(b)], b, base)
+        np.testing.assert_allclose(rows, dense, rtol=1e-10, atol=1e-12)
+
+
+def test_zero_keys_give_uniform_weights_over_the_visible_set():
+    """K = 0 makes every score 0, so each output is the plain mean of the
+    visible V rows, counting duplicates; with V encoding the position, the
+    output reveals exactly which keys a row saw (K = 0 is RoPE-invariant)."""
+    N, b, chunk, sink, d, base = 3, 64, 16, 32, 8, 500000.0
+    L = N * b
+    q = _bf(_rand((L, 2, d), 7))
+    k = np.zeros((L, 1, d))
+    v = np.zeros((L, 1, d))
+    v[:, 0, 0] = np.arange(L)
+    v[:, 0, 1] = np.arange(L) ** 2
+    sel = np.array([[0, 2], [1, 3], [0, 1]])
+    pre = S.prefix_positions(sel, N, b, chunk, sink)
+    k_hat = A.rotate_bf16(k, np.arange(L), base)
+    for i in range(N):
+        for r in [0, 1, 17, b - 1]:
+            keys = list(pre[i]) + list(range(i * b, i * b + r + 1))
+            o = A.phase1_rows(q, k_hat, v, pre, [(i, r)], b, base)[0]
+            assert o[0, 0] == pytest.approx(np.mean(keys), rel=1e-12)
+            assert o[1, 1] == pytest.approx(np.mean(np.square(keys)), rel=1e-12)
+    # Phase 2: lse of a shard of n keys with zero scores is ln n
+    kc = np.zeros((2, 1, 40, d))
+    vc = _rand((2, 1, 40, d), 8)
+    parts = A.phase2_partials(_rand((3, 2, d), 9), 1000, kc, vc, None, None, base)
+    for o, lse in parts:
+        np.testing.assert_allclose(lse, math.log(40), rtol=1e-12)
+
+
+def _phase2_case(seed, n_shards=3, n=37, lq=5, hq=4, hkv=2, d=16, base=500000.0):
+    rng = np.random.default_rng(seed)
+    kc = _bf(rng.standard_normal((n_shards, hkv, n, d)))
+    vc = _bf(rng.standard_normal((n_shards, hkv, n, d)))
+    qq = _bf(rng.standard_normal((lq, hq, d)))
+    ks = _bf(rng.standard_normal((lq, hkv, d)))
+    vs = _bf(rng.standard_normal((lq, hkv, d)))
+    return qq, kc, vc, ks, vs, base
+
+
+@pytest.mark.parametrize("with_self", [True, False])
+def test_lse_merge_of_shards_equals_dense_attention(with_self):
+    """Section 2.2: the merge of per-shard partials is exact attention over all
+    retained shards (plus the causal self shard)."""
+    qq, kc, vc, ks, vs, base = _phase2_case(10)
+    if not with_self:
+        ks = vs = None
+    parts = A.phase2_partials(qq, 5000, kc, vc, ks, vs, base)
+    o, lse = A.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+    o2, lse2 = A.dense_query_attention(qq, 5000, kc, vc, ks, vs, base)
+    np.testing.assert_allclose(o, o2, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-12, atol=1e-12)
+
+
+def test_merge_is_independent_of_shard_order_and_split_points():
+    qq, kc, vc, ks, vs, base = _phase2_case(11, n_shards=2, n=40)
+    whole = A.phase2_partials(qq, 100, kc, vc, None, None, base)
+    o1, l1 = A.lse_merge([p[0] for p in whole], [p[1] for p in whole])
+    # split every shard at an arbitrary point and reverse the order
+    pieces_k = [kc[s][:, a:b_] for s in range(2) for (a, b_) in [(0, 13), (13, 40)]][::-1]
+    pieces_v = [vc[s][:, a:b_] for s in range(2) for (a, b_) in [(0, 13), (13, 40)]][::-1]
+    parts = []
+    for pk, pv in zip(pieces_k, pieces_v):
+        parts += A.phase2_partials(qq, 100, pk[None], pv[None], None, None, base)
+    o2, l2 = A.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+    np.testing.assert_allclose(o1, o2, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12)
+
+
+def test_one_shard_is_plain_attention_and_lse_is_logsumexp():
+    qq, kc, vc, ks, vs, base = _phase2_case(12, n_shards=1)
+    (o, lse), = A.phase2_partials(qq, 77, kc, vc, None, None, base)
+    lq, hq, d = qq.shape
+    q_hat = A.rotate_bf16(qq, 77 + np.arange(lq), base)
+    qh = torch.from_numpy(q_hat).permute(1, 0, 2)[None]
+    kh = torch.from_numpy(kc[0])[None]
+    vh = torch.from_numpy(vc[0])[None]
+    want = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, enable_gqa=True)
+    np.testing.assert_allclose(o, want[0].permute(1, 0, 2).numpy(), rtol=1e-10, atol=1e-12)
+    for h in range(hq):
+        s = q_hat[:, h, :] @ kc[0, h // 2].T / math.sqrt(d)
+        np.testing.assert_allclose(lse[:, h], logsumexp(s, axis=1), rtol=1e-12)
+
+
+def test_self_shard_is_causal():
+    """The first query token sees only itself among the query tokens, so with a
+    single self key its self-shard output is that key's value row."""
+    qq, kc, vc, ks, vs, base = _phase2_case(13)
+    parts = A.phase2_partials(qq, 9000, kc, vc, ks, vs, base)
+    o_self, lse_self = parts[-1]
+    for h in range(qq.shape[1]):
+        np.testing.assert_allclose(o_self[0, h], vs[0, h // 2], rtol=1e-12)
+
+
+def test_retained_cache_does_not_depend_on_selection():
+    """The kept KV is the block's own rotated keys and values whatever the
+    prefix (Section 2.2: the retained cache is identical to Star Attention's)."""
+    N, b, d, base = 2, 32, 8, 500000.0
+    k, v = _bf(_rand((N * b, 2, d), 14)), _bf(_rand((N * b, 2, d), 15))
+    kc, vc = A.retained_cache(k, v, N, b, base)
+    assert kc.shape == (N, 2, b, d)
+    np.testing.assert_array_equal(vc[1, 0], v[b:, 0])
+    np.testing.assert_array_equal(kc[1, 1, 3], A.rotate_bf16(k[b + 3:b + 4], [b + 3], base)[0, 1])
