@@ -1,0 +1,164 @@
+/*
+ * pulsar.h -- C ABI of the Pulsar Attention hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the method's own statement of the problem in "Dropping the
+ * Anchor: Statistical Context Summarization for Distributed Systems via Pulsar
+ * Attention":
+ *   pulsar_select         Section 2.1: Max-IDF summary selection from token IDs
+ *   pulsar_phase1_encode  Section 2 / 2.1: each block attends over
+ *                         [sink || summaries of earlier blocks || own block] at
+ *                         original positions and keeps only its own KV
+ *   pulsar_phase2_query   Section 2.2: the query attends to every retained shard
+ *                         (local attention per shard, partial results out)
+ *   pulsar_lse_merge      Section 2.2 and the Star Attention review's distributed
+ *                         online-softmax aggregation: exact log-sum-exp merge
+ * All "hosts" of the method are one batched launch on one GPU.
+ *
+ * Conventions shared by every call
+ *  - Tensor arguments are DEVICE pointers owned by the caller.  bf16 tensors are
+ *    passed as their raw 16-bit patterns (uint16_t).  Layouts are row-major in
+ *    the bracketed order.  Every tensor pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on that stream and returns; nothing synchronises the host.
+ *  - Return value: PULSAR_OK or a negative PULSAR_E* code.  Arguments are
+ *    validated on the host before anything is enqueued, so an error return
+ *    means nothing was launched (except PULSAR_EHIP, which reports a launch
+ *    error raised after work was enqueued).  No call prints, throws or exits.
+ *  - The library allocates no device memory.  Scratch space is the caller's
+ *    workspace (size from pulsar_workspace_bytes); calls that share one
+ *    workspace must be ordered on one stream.
+ *  - Query head h reads KV head h / (n_q_heads / n_kv_heads) (grouped heads).
+ *  - RoPE is the rotate-half form with inverse frequencies base^(-2i/d),
+ *    angles derived in float64; rotated keys/queries are rounded to bf16.
+ */
+#ifndef PULSAR_H
+#define PULSAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PULSAR_OK 0
+#define PULSAR_EINVAL -1      /* bad geometry, null or misaligned pointer */
+#define PULSAR_EWORKSPACE -2  /* workspace missing or smaller than required */
+#define PULSAR_EHIP -3        /* the HIP runtime reported an error */
+#define PULSAR_EUNSUPPORTED -4 /* valid request outside what the kernels implement */
+
+/* Context geometry of one sequence.
+ *   n_blocks      N >= 1 blocks ("hosts"), each of block_size tokens; L = N * block_size
+ *   block_size    b, a multiple of chunk_size and of 64
+ *   chunk_size    tokens per chunk; 32 is the method's value (the only one supported)
+ *   budget_chunks k chunks kept per block (12.5 % of b is k = b / 256); k >= n_chunks
+ *                 keeps every chunk; 0 keeps none (Star Attention's anchor setting)
+ *   sink_size     S first tokens of the sequence prepended to every block i > 0;
+ *                 a multiple of chunk_size, 0 <= S <= L
+ *   vocab_size    V, token ids must lie in [0, V); V <= 1,048,576
+ */
+typedef struct pulsar_geom {
+  int32_t n_blocks;
+  int32_t block_size;
+  int32_t chunk_size;
+  int32_t budget_chunks;
+  int32_t sink_size;
+  int32_t vocab_size;
+} pulsar_geom;
+
+/* Attention geometry.  head_dim 64 or 128; n_q_heads a multiple of n_kv_heads. */
+typedef struct pulsar_attn {
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t reserved;   /* must be 0 */
+  double rope_base;   /* > 1, e.g. 500000 */
+} pulsar_attn;
+
+/* Bytes of workspace pulsar_select and pulsar_phase1_encode need for this
+ * geometry (one workspace serves both).  Returns 0 if the geometry is invalid. */
+size_t pulsar_workspace_bytes(const pulsar_geom* g, const pulsar_attn* a);
+
+/* Number of chunks kept per block: min(budget_chunks, block_size / chunk_size). */
+int32_t pulsar_kept_chunks(const pulsar_geom* g);
+
+/* Max-IDF summary selection ("Dropping the Anchor ..." Section 2.1, Figure 2).
+ * Each block is a document; df(t) = number of blocks containing token t (all N
+ * blocks); each chunk is scored by its rarest token, max idf = log(N / min df),
+ * so the kernel ranks chunks by the integer min df; the k best chunks of each
+ * block (lowest min df, earlier chunk first among equals) are returned in
+ * ascending chunk order.
+ *   tok          [L] int32 token ids
+ *   sel          [N][kept] int32 out: chunk indices within the block, ascending
+ *   chunk_min_df [N][n_chunks] int32 out, or NULL
+ *   df           [V] int32 out, or NULL
+ *   ws           workspace of at least pulsar_workspace_bytes(g, NULL-safe a) bytes;
+ *                its first 4 bytes become a status word: 0, or 1 if some token id
+ *                was outside [0, V) (such ids are skipped by the count)
+ * Errors: PULSAR_EINVAL, PULSAR_EWORKSPACE, PULSAR_EUNSUPPORTED, PULSAR_EHIP. */
+int pulsar_select(const pulsar_geom* g, const int32_t* tok, int32_t* sel,
+                  int32_t* chunk_min_df, int32_t* df, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* Phase-1 context encoding ("Dropping the Anchor ..." Section 2 and 2.1).
+ * Block i > 0 attends over [first S tokens || kept chunks of blocks 0..i-1 in
+ * order || own block], causally, every token at its original position; block
+ * 0 attends over itself only.  Prefix entries are not de-duplicated.  Only the
+ * block rows are queries.  The kept KV is the block's own keys (rotated, bf16)
+ * and values.
+ *   q        [L][Hq][d] bf16, pre-RoPE
+ *   k, v     [L][Hkv][d] bf16, pre-RoPE keys and values
+ *   sel      [N][kept] int32 from pulsar_select (ascending within each block)
+ *   o        [L][Hq][d] float32 out: attention output of every block row
+ *   k_cache  [N][Hkv][b][d] bf16 out: RoPE(k) rounded to bf16
+ *   v_cache  [N][Hkv][b][d] bf16 out: v
+ *   ws       workspace (pulsar_workspace_bytes); ws_bytes its size
+ * Errors: PULSAR_EINVAL, PULSAR_EWORKSPACE, PULSAR_EUNSUPPORTED, PULSAR_EHIP. */
+int pulsar_phase1_encode(const pulsar_geom* g, const pulsar_attn* a, const uint16_t* q,
+                         const uint16_t* k, const uint16_t* v, const int32_t* sel,
+                         float* o, uint16_t* k_cache, uint16_t* v_cache, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Number of partial results pulsar_phase2_query writes per sequence for this
+ * shape: every shard is split into the same number of contiguous key ranges,
+ * plus one part for the self shard when has_self != 0.  Returns <= 0 on error. */
+int32_t pulsar_phase2_num_parts(const pulsar_attn* a, int32_t batch, int32_t n_shards,
+                                int32_t shard_len, int32_t q_len, int32_t has_self);
+
+/* Phase-2 query attention over retained shards ("Dropping the Anchor ..."
+ * Section 2.2).  Query token t of sequence s sits at position q_pos0 + t.  For
+ * every part (a contiguous key range of one shard, or the self shard) the call
+ * writes the softmax-normalised partial output and its log-sum-exp (natural
+ * log of sum exp(q.k / sqrt(d)) over the part's keys).  The self shard holds
+ * the query tokens' own keys and values, attended causally (token t sees self
+ * keys 0..t); pass k_self = v_self = NULL to attend to the retained shards only.
+ *   qq               [B][Lq][Hq][d] bf16, pre-RoPE
+ *   k_cache, v_cache [B][n_shards][Hkv][shard_len][d] bf16 (keys already rotated)
+ *   k_self, v_self   [B][Lq][Hkv][d] bf16 pre-RoPE, or both NULL
+ *   o_part           [B][n_parts][Lq][Hq][d] float32 out
+ *   lse_part         [B][n_parts][Lq][Hq] float32 out
+ *   n_parts          must equal pulsar_phase2_num_parts(...) for this shape
+ * Errors: PULSAR_EINVAL, PULSAR_EUNSUPPORTED, PULSAR_EHIP. */
+int pulsar_phase2_query(const pulsar_attn* a, int32_t batch, int32_t n_shards,
+                        int32_t shard_len, const uint16_t* qq, int32_t q_len,
+                        int64_t q_pos0, const uint16_t* k_cache, const uint16_t* v_cache,
+                        const uint16_t* k_self, const uint16_t* v_self, float* o_part,
+                        float* lse_part, int32_t n_parts, void* stream);
+
+/* Exact log-sum-exp merge of partial attention results (the Star Attention
+ * review's corrected update: weight exp(s_h - s_global) on the normalised A_h):
+ *   lse = ln sum_p exp(lse_part[p]),  o = sum_p exp(lse_part[p] - lse) * o_part[p]
+ *   o_part [B][n_parts][Lq][Hq][d] float32, lse_part [B][n_parts][Lq][Hq] float32
+ *   o      [B][Lq][Hq][d] float32 out, lse [B][Lq][Hq] float32 out (may be NULL)
+ * Errors: PULSAR_EINVAL, PULSAR_EHIP. */
+int pulsar_lse_merge(int32_t batch, int32_t n_parts, int32_t q_len, int32_t n_q_heads,
+                     int32_t head_dim, const float* o_part, const float* lse_part, float* o,
+                     float* lse, void* stream);
+
+/* Static description of an error code. */
+const char* pulsar_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PULSAR_H */

@@ -1,0 +1,203 @@
+// C ABI of the Pulsar hot path: host-side validation, workspace carving and
+// launches on the caller's stream.  Declarations and contracts: include/pulsar.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/pulsar.h"
+#include "launch.hpp"
+
+using namespace pulsar;
+
+namespace {
+
+constexpr int64_t kMaxVocab = 1 << 20;
+constexpr int64_t kMaxContext = int64_t(1) << 30;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t kept_chunks(const pulsar_geom* g) {
+  const int32_t n_chunks = g->block_size / g->chunk_size;
+  return g->budget_chunks < n_chunks ? g->budget_chunks : n_chunks;
+}
+
+int check_geom(const pulsar_geom* g) {
+  if (!g) return PULSAR_EINVAL;
+  if (g->n_blocks < 1 || g->block_size < 1 || g->chunk_size < 1 || g->budget_chunks < 0 ||
+      g->sink_size < 0 || g->vocab_size < 1)
+    return PULSAR_EINVAL;
+  if (g->block_size % g->chunk_size != 0) return PULSAR_EINVAL;
+  const int64_t L = (int64_t)g->n_blocks * g->block_size;
+  if (L > kMaxContext) return PULSAR_EUNSUPPORTED;
+  if (g->vocab_size > kMaxVocab) return PULSAR_EUNSUPPORTED;
+  if (g->sink_size > L) return PULSAR_EINVAL;
+  const int64_t n_chunks = g->block_size / g->chunk_size;
+  if (n_chunks + g->n_blocks + 2 > 40000) return PULSAR_EUNSUPPORTED;  // LDS of the top-k kernel
+  const int64_t p_last = (int64_t)g->sink_size +
+                         (int64_t)g->chunk_size * kept_chunks(g) * (g->n_blocks - 1);
+  if (p_last > (int64_t(1) << 30)) return PULSAR_EUNSUPPORTED;
+  return PULSAR_OK;
+}
+
+int check_attn(const pulsar_attn* a) {
+  if (!a) return PULSAR_EINVAL;
+  if (a->n_q_heads < 1 || a->n_kv_heads < 1 || a->reserved != 0) return PULSAR_EINVAL;
+  if (a->n_q_heads % a->n_kv_heads != 0) return PULSAR_EINVAL;
+  if (!(a->rope_base > 1.0) || !isfinite(a->rope_base)) return PULSAR_EINVAL;
+  if (a->head_dim != 64 && a->head_dim != 128) return PULSAR_EUNSUPPORTED;
+  const int group = a->n_q_heads / a->n_kv_heads;
+  if (!(group == 1 || group == 2 || group % 4 == 0)) return PULSAR_EUNSUPPORTED;
+  return PULSAR_OK;
+}
+
+struct Layout {
+  size_t status, df, rope, order, total;
+};
+
+Layout layout(const pulsar_geom* g, const pulsar_attn* a) {
+  Layout l{};
+  size_t off = 0;
+  l.status = off;
+  off += kAlign;
+  l.df = off;
+  off = align_up(off + (size_t)g->vocab_size * 4);
+  const int64_t L = (int64_t)g->n_blocks * g->block_size;
+  l.rope = off;
+  if (a) off = align_up(off + (size_t)L * (a->head_dim / 2) * 8);
+  l.order = off;
+  if (a) {
+    Phase1Geometry pg = phase1_geometry(g->n_blocks, g->block_size, g->chunk_size,
+                                        kept_chunks(g), g->sink_size, a->n_q_heads,
+                                        a->n_kv_heads, a->head_dim);
+    off = align_up(off + (size_t)pg.n_blocks * pg.n_row_tiles * 4);
+  }
+  l.total = off;
+  return l;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+size_t pulsar_workspace_bytes(const pulsar_geom* g, const pulsar_attn* a) {
+  if (check_geom(g) != PULSAR_OK) return 0;
+  if (a && check_attn(a) != PULSAR_OK) return 0;
+  return layout(g, a).total;
+}
+
+int32_t pulsar_kept_chunks(const pulsar_geom* g) {
+  if (check_geom(g) != PULSAR_OK) return -1;
+  return kept_chunks(g);
+}
+
+int pulsar_select(const pulsar_geom* g, const int32_t* tok, int32_t* sel, int32_t* chunk_min_df,
+                  int32_t* df, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_geom(g);
+  if (rc) return rc;
+  const int32_t kept = kept_chunks(g);
+  if (!aligned16(tok)) return PULSAR_EINVAL;
+  if (kept > 0 && !aligned16(sel)) return PULSAR_EINVAL;
+  if (chunk_min_df && !aligned16(chunk_min_df)) return PULSAR_EINVAL;
+  if (df && !aligned16(df)) return PULSAR_EINVAL;
+  const Layout l = layout(g, nullptr);
+  if (!ws || ws_bytes < l.total) return PULSAR_EWORKSPACE;
+  if (!aligned16(ws)) return PULSAR_EINVAL;
+  char* w = static_cast<char*>(ws);
+  int32_t* status = reinterpret_cast<int32_t*>(w + l.status);
+  int32_t* dfp = df ? df : reinterpret_cast<int32_t*>(w + l.df);
+  return launch_select(tok, g->n_blocks, g->block_size, g->chunk_size, kept, g->vocab_size, sel,
+                       chunk_min_df, dfp, status, as_stream(stream)) == 0
+             ? PULSAR_OK
+             : PULSAR_EHIP;
+}
+
+int pulsar_phase1_encode(const pulsar_geom* g, const pulsar_attn* a, const uint16_t* q,
+                         const uint16_t* k, const uint16_t* v, const int32_t* sel, float* o,
+                         uint16_t* k_cache, uint16_t* v_cache, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int rc = check_geom(g);
+  if (rc) return rc;
+  rc = check_attn(a);
+  if (rc) return rc;
+  const int32_t kept = kept_chunks(g);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return PULSAR_EINVAL;
+  if (g->n_blocks > 1 && kept > 0 && !aligned16(sel)) return PULSAR_EINVAL;
+  const Layout l = layout(g, a);
+  if (!ws || ws_bytes < l.total) return PULSAR_EWORKSPACE;
+  if (!aligned16(ws)) return PULSAR_EINVAL;
+  char* w = static_cast<char*>(ws);
+  float* rope_cs = reinterpret_cast<float*>(w + l.rope);
+  int32_t* order = reinterpret_cast<int32_t*>(w + l.order);
+  const int64_t L = (int64_t)g->n_blocks * g->block_size;
+  hipStream_t s = as_stream(stream);
+  if (launch_rope_fill(k, v, L, g->block_size, a->n_kv_heads, a->head_dim, a->rope_base, rope_cs,
+                       k_cache, v_cache, s))
+    return PULSAR_EHIP;
+  Phase1Geometry pg = phase1_geometry(g->n_blocks, g->block_size, g->chunk_size, kept,
+                                      g->sink_size, a->n_q_heads, a->n_kv_heads, a->head_dim);
+  if (launch_phase1(pg, q, k_cache, v_cache, sel, rope_cs, order, o, s)) return PULSAR_EHIP;
+  return PULSAR_OK;
+}
+
+int32_t pulsar_phase2_num_parts(const pulsar_attn* a, int32_t batch, int32_t n_shards,
+                                int32_t shard_len, int32_t q_len, int32_t has_self) {
+  if (check_attn(a) != PULSAR_OK) return PULSAR_EINVAL;
+  if (batch < 1 || n_shards < 0 || q_len < 1) return PULSAR_EINVAL;
+  if (n_shards > 0 && shard_len < 1) return PULSAR_EINVAL;
+  if (n_shards == 0 && !has_self) return PULSAR_EINVAL;
+  Phase2Geometry pg = phase2_geometry(batch, n_shards, n_shards > 0 ? shard_len : 1, q_len,
+                                      a->n_q_heads, a->n_kv_heads, a->head_dim, has_self);
+  return pg.n_parts;
+}
+
+int pulsar_phase2_query(const pulsar_attn* a, int32_t batch, int32_t n_shards, int32_t shard_len,
+                        const uint16_t* qq, int32_t q_len, int64_t q_pos0,
+                        const uint16_t* k_cache, const uint16_t* v_cache, const uint16_t* k_self,
+                        const uint16_t* v_self, float* o_part, float* lse_part, int32_t n_parts,
+                        void* stream) {
+  const int has_self = k_self != nullptr || v_self != nullptr;
+  const int32_t want = pulsar_phase2_num_parts(a, batch, n_shards, shard_len, q_len, has_self);
+  if (want <= 0) return want < 0 ? want : PULSAR_EINVAL;
+  if (n_parts != want) return PULSAR_EINVAL;
+  if (has_self && (!aligned16(k_self) || !aligned16(v_self))) return PULSAR_EINVAL;
+  if (!aligned16(qq) || !aligned16(o_part) || !lse_part) return PULSAR_EINVAL;
+  if (n_shards > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) return PULSAR_EINVAL;
+  if (q_pos0 < 0) return PULSAR_EINVAL;
+  Phase2Geometry pg = phase2_geometry(batch, n_shards, n_shards > 0 ? shard_len : 1, q_len,
+                                      a->n_q_heads, a->n_kv_heads, a->head_dim, has_self);
+  return launch_phase2(pg, qq, q_pos0, k_cache, v_cache, k_self, v_self, a->rope_base, o_part,
+                       lse_part, as_stream(stream)) == 0
+             ? PULSAR_OK
+             : PULSAR_EHIP;
+}
+
+int pulsar_lse_merge(int32_t batch, int32_t n_parts, int32_t q_len, int32_t n_q_heads,
+                     int32_t head_dim, const float* o_part, const float* lse_part, float* o,
+                     float* lse, void* stream) {
+  if (batch < 1 || n_parts < 1 || q_len < 1 || n_q_heads < 1) return PULSAR_EINVAL;
+  if (head_dim != 64 && head_dim != 128) return PULSAR_EUNSUPPORTED;
+  if (!aligned16(o_part) || !lse_part || !aligned16(o)) return PULSAR_EINVAL;
+  return launch_merge(batch, n_parts, q_len, n_q_heads, head_dim, o_part, lse_part, o, lse,
+                      as_stream(stream)) == 0
+             ? PULSAR_OK
+             : PULSAR_EHIP;
+}
+
+const char* pulsar_strerror(int code) {
+  switch (code) {
+    case PULSAR_OK: return "ok";
+    case PULSAR_EINVAL: return "invalid argument (geometry, null or misaligned pointer)";
+    case PULSAR_EWORKSPACE: return "workspace missing or too small";
+    case PULSAR_EHIP: return "HIP runtime error while launching";
+    case PULSAR_EUNSUPPORTED: return "valid request outside what the kernels implement";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

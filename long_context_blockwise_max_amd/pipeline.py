@@ -1,0 +1,134 @@
+"""Host-side orchestration of the whole hot path on one GPU.
+
+`HotPath` owns the device buffers of one problem and enqueues, on one stream,
+the four C-ABI calls in the method's order: Max-IDF selection, Phase-1
+encoding (which also fills the retained cache), Phase-2 query attention over
+every retained shard plus the query's own causal shard, and the exact LSE
+merge.  torch is used for device memory and the stream only.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import binding as B
+
+
+@dataclass(frozen=True)
+class Geometry:
+    n_blocks: int
+    block_size: int
+    chunk_size: int
+    budget_chunks: int
+    sink_size: int
+    vocab_size: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    q_len: int
+    batch: int = 1
+    rope_base: float = 500000.0
+    with_self: bool = True
+
+    @property
+    def context_len(self):
+        return self.n_blocks * self.block_size
+
+
+def _bf16_empty(shape, device):
+    return torch.empty(shape, dtype=torch.bfloat16, device=device)
+
+
+class HotPath:
+    """Device buffers + the four calls.  Sequence 0 of the Phase-2 batch is
+    the sequence Phase 1 encodes (its retained cache is written in place into
+    slot 0 of the batched cache); further sequences' caches are inputs."""
+
+    def __init__(self, geo: Geometry, device="cuda"):
+        self.geo = geo
+        g = geo
+        dev = torch.device(device)
+        self.device = dev
+        L, hq, hkv, d = g.context_len, g.n_q_heads, g.n_kv_heads, g.head_dim
+        self.cgeom = B.make_geom(g.n_blocks, g.block_size, g.chunk_size, g.budget_chunks,
+                                 g.sink_size, g.vocab_size)
+        self.cattn = B.make_attn(hq, hkv, d, g.rope_base)
+        self.kept = B.pulsar_kept_chunks(self.cgeom)
+        if self.kept < 0:
+            raise B.PulsarError(B.PULSAR_EINVAL, "geometry")
+        n_chunks = g.block_size // g.chunk_size
+        ws_bytes = B.pulsar_workspace_bytes(self.cgeom, self.cattn)
+        if ws_bytes == 0:
+            raise B.PulsarError(B.PULSAR_EINVAL, "pulsar_workspace_bytes")
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        self.tok = torch.empty(L, dtype=torch.int32, device=dev)
+        self.sel = torch.empty((g.n_blocks, max(self.kept, 1)), dtype=torch.int32, device=dev)
+        self.chunk_min_df = torch.empty((g.n_blocks, n_chunks), dtype=torch.int32, device=dev)
+        self.df = torch.empty(g.vocab_size, dtype=torch.int32, device=dev)
+        self.q = _bf16_empty((L, hq, d), dev)
+        self.k = _bf16_empty((L, hkv, d), dev)
+        self.v = _bf16_empty((L, hkv, d), dev)
+        self.o = torch.empty((L, hq, d), dtype=torch.float32, device=dev)
+        self.k_cache = _bf16_empty((g.batch, g.n_blocks, hkv, g.block_size, d), dev)
+        self.v_cache = _bf16_empty((g.batch, g.n_blocks, hkv, g.block_size, d), dev)
+        self.qq = _bf16_empty((g.batch, g.q_len, hq, d), dev)
+        self.k_self = _bf16_empty((g.batch, g.q_len, hkv, d), dev) if g.with_self else None
+        self.v_self = _bf16_empty((g.batch, g.q_len, hkv, d), dev) if g.with_self else None
+        self.n_parts = B.pulsar_phase2_num_parts(self.cattn, g.batch, g.n_blocks, g.block_size,
+                                                 g.q_len, g.with_self)
+        self.o_part = torch.empty((g.batch, self.n_parts, g.q_len, hq, d), dtype=torch.float32,
+                                  device=dev)
+        self.lse_part = torch.empty((g.batch, self.n_parts, g.q_len, hq), dtype=torch.float32,
+                                    device=dev)
+        self.o_q = torch.empty((g.batch, g.q_len, hq, d), dtype=torch.float32, device=dev)
+        self.lse_q = torch.empty((g.batch, g.q_len, hq), dtype=torch.float32, device=dev)
+
+    # inputs -------------------------------------------------------------
+    @staticmethod
+    def _bits_to_dev(dst, bits):
+        t = torch.from_numpy(bits.view("int16")).view(torch.bfloat16)
+        dst.copy_(t.reshape(dst.shape))
+
+    def upload(self, tok=None, q=None, k=None, v=None, qq=None, k_self=None, v_self=None):
+        """Copy host arrays (int32 tokens; bf16 bit patterns as uint16) to the device."""
+        if tok is not None:
+            self.tok.copy_(torch.from_numpy(tok.astype("int32")))
+        for dst, src in ((self.q, q), (self.k, k), (self.v, v), (self.qq, qq),
+                         (self.k_self, k_self), (self.v_self, v_self)):
+            if src is not None and dst is not None:
+                self._bits_to_dev(dst, src)
+
+    def upload_extra_cache(self, seq, k_bits, v_bits):
+        self._bits_to_dev(self.k_cache[seq], k_bits)
+        self._bits_to_dev(self.v_cache[seq], v_bits)
+
+    # the four calls -------------------------------------------------------
+    def select(self, stream=None):
+        B.pulsar_select(self.cgeom, self.tok, self.sel if self.kept > 0 else None,
+                        self.chunk_min_df, self.df, self.ws, stream)
+
+    def phase1(self, stream=None):
+        B.pulsar_phase1_encode(self.cgeom, self.cattn, self.q, self.k, self.v,
+                               self.sel if self.kept > 0 else None, self.o,
+                               self.k_cache[0], self.v_cache[0], self.ws, stream)
+
+    def phase2(self, stream=None):
+        g = self.geo
+        B.pulsar_phase2_query(self.cattn, g.batch, g.n_blocks, g.block_size, self.qq, g.q_len,
+                              g.context_len, self.k_cache, self.v_cache, self.k_self, self.v_self,
+                              self.o_part, self.lse_part, self.n_parts, stream)
+
+    def merge(self, stream=None):
+        g = self.geo
+        B.pulsar_lse_merge(g.batch, self.n_parts, g.q_len, g.n_q_heads, g.head_dim, self.o_part,
+                           self.lse_part, self.o_q, self.lse_q, stream)
+
+    def step(self, stream=None):
+        self.select(stream)
+        self.phase1(stream)
+        self.phase2(stream)
+        self.merge(stream)
+
+    def status_word(self) -> int:
+        return int(self.ws[:4].view(torch.int32).item())

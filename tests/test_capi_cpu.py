@@ -1,0 +1,142 @@
+"""The C-ABI library loads without a GPU, exports every declared entry point,
+and rejects bad arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_blockwise_max_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pulsar.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libpulsar.so not built")
+
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced: validation fails first
+FAKE_MIS = ctypes.c_void_p(0x10008)      # not 16-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(pulsar_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for n in ("pulsar_select", "pulsar_phase1_encode", "pulsar_phase2_query", "pulsar_lse_merge"):
+        assert n in names
+    assert set(names) == set(B.EXPORTED)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def geom(**kw):
+    d = dict(n_blocks=8, block_size=16384, chunk_size=32, budget_chunks=64, sink_size=64,
+             vocab_size=128256)
+    d.update(kw)
+    return B.make_geom(**d)
+
+
+ATTN = B.make_attn(32, 8, 128, 500000.0)
+
+
+@needs_lib
+def test_workspace_and_kept_chunks():
+    g = geom()
+    assert B.pulsar_kept_chunks(g) == 64
+    assert B.pulsar_kept_chunks(geom(budget_chunks=10 ** 6)) == 512
+    ws_sel = B.pulsar_workspace_bytes(g, None)
+    ws_all = B.pulsar_workspace_bytes(g, ATTN)
+    assert ws_sel >= 128256 * 4
+    # rotary table (L x d/2 float2) + work order fit in the full workspace
+    assert ws_all >= ws_sel + 131072 * 64 * 8
+    assert B.pulsar_workspace_bytes(geom(block_size=100), ATTN) == 0    # not a chunk multiple
+    assert B.pulsar_workspace_bytes(g, B.make_attn(32, 8, 96, 5e5)) == 0   # head_dim
+    assert B.pulsar_workspace_bytes(g, B.make_attn(30, 8, 128, 5e5)) == 0  # Hq % Hkv
+
+
+@needs_lib
+@pytest.mark.parametrize("bad", [
+    dict(n_blocks=0), dict(block_size=0), dict(chunk_size=0), dict(budget_chunks=-1),
+    dict(sink_size=-1), dict(vocab_size=0), dict(block_size=100), dict(sink_size=10 ** 9),
+])
+def test_select_rejects_bad_geometry(bad):
+    lib = B.lib()
+    rc = lib.pulsar_select(ctypes.byref(geom(**bad)), FAKE, FAKE, None, None, FAKE, 1 << 30, None)
+    assert rc == B.PULSAR_EINVAL
+
+
+@needs_lib
+def test_select_rejects_pointers_and_small_workspace():
+    lib = B.lib()
+    g = geom()
+    assert lib.pulsar_select(ctypes.byref(g), None, FAKE, None, None, FAKE, 1 << 30, None) == B.PULSAR_EINVAL
+    assert lib.pulsar_select(ctypes.byref(g), FAKE_MIS, FAKE, None, None, FAKE, 1 << 30, None) == B.PULSAR_EINVAL
+    assert lib.pulsar_select(ctypes.byref(g), FAKE, FAKE, None, None, FAKE, 16, None) == B.PULSAR_EWORKSPACE
+    assert lib.pulsar_select(ctypes.byref(g), FAKE, FAKE, None, None, None, 1 << 30, None) == B.PULSAR_EWORKSPACE
+    big = geom(vocab_size=(1 << 20) + 1)
+    assert lib.pulsar_select(ctypes.byref(big), FAKE, FAKE, None, None, FAKE, 1 << 30, None) == B.PULSAR_EUNSUPPORTED
+
+
+@needs_lib
+def test_phase1_rejects_bad_arguments():
+    lib = B.lib()
+    g = geom()
+    args = [FAKE] * 7
+    ws = B.pulsar_workspace_bytes(g, ATTN)
+
+    def call(gg, aa, ptrs, wsb):
+        return lib.pulsar_phase1_encode(ctypes.byref(gg), ctypes.byref(aa), *ptrs, FAKE, wsb, None)
+
+    assert call(g, ATTN, args, ws - 1) == B.PULSAR_EWORKSPACE
+    assert call(g, B.make_attn(32, 8, 80, 5e5), args, ws) == B.PULSAR_EUNSUPPORTED
+    assert call(g, B.make_attn(24, 8, 128, 5e5), args, ws) == B.PULSAR_EUNSUPPORTED  # group of 3
+    assert call(g, B.make_attn(32, 8, 128, 1.0), args, ws) == B.PULSAR_EINVAL
+    bad = B.make_attn(32, 8, 128, 5e5)
+    bad.reserved = 1
+    assert call(g, bad, args, ws) == B.PULSAR_EINVAL
+    for i in range(7):
+        p = list(args)
+        p[i] = None if i != 4 else FAKE_MIS
+        assert call(g, ATTN, p, ws) == B.PULSAR_EINVAL, i
+
+
+@needs_lib
+def test_phase2_part_count_and_rejections():
+    n = B.pulsar_phase2_num_parts(ATTN, 1, 8, 16384, 64, True)
+    assert n >= 9 and (n - 1) % 8 == 0
+    n0 = B.pulsar_phase2_num_parts(ATTN, 1, 8, 16384, 64, False)
+    assert n0 == n - 1
+    assert B.pulsar_phase2_num_parts(ATTN, 8, 16, 32768, 1, True) >= 17
+    # tiny shards never get an empty part
+    for shard_len in (1, 63, 64, 65, 200):
+        nn = B.pulsar_phase2_num_parts(ATTN, 1, 2, shard_len, 4, False)
+        assert nn // 2 <= (shard_len + 63) // 64
+    lib = B.lib()
+    with pytest.raises(B.PulsarError):
+        B.pulsar_phase2_num_parts(ATTN, 0, 8, 16384, 64, True)
+    rc = lib.pulsar_phase2_query(ctypes.byref(ATTN), 1, 8, 16384, FAKE, 64, 131072, FAKE, FAKE,
+                                 FAKE, FAKE, FAKE, FAKE, n + 1, None)
+    assert rc == B.PULSAR_EINVAL                      # wrong part count
+    rc = lib.pulsar_phase2_query(ctypes.byref(ATTN), 1, 8, 16384, FAKE, 64, 131072, FAKE, FAKE,
+                                 FAKE, None, FAKE, FAKE, n, None)
+    assert rc == B.PULSAR_EINVAL                      # k_self without v_self
+    rc = lib.pulsar_phase2_query(ctypes.byref(ATTN), 1, 8, 16384, FAKE, 64, -1, FAKE, FAKE,
+                                 FAKE, FAKE, FAKE, FAKE, n, None)
+    assert rc == B.PULSAR_EINVAL                      # negative position
+
+
+@needs_lib
+def test_merge_rejections_and_strerror():
+    lib = B.lib()
+    assert lib.pulsar_lse_merge(0, 4, 64, 32, 128, FAKE, FAKE, FAKE, None, None) == B.PULSAR_EINVAL
+    assert lib.pulsar_lse_merge(1, 4, 64, 32, 96, FAKE, FAKE, FAKE, None, None) == B.PULSAR_EUNSUPPORTED
+    assert lib.pulsar_lse_merge(1, 4, 64, 32, 128, FAKE_MIS, FAKE, FAKE, None, None) == B.PULSAR_EINVAL
+    for c in (0, -1, -2, -3, -4, 7):
+        assert isinstance(B.strerror(c), str) and B.strerror(c)

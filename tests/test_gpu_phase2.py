@@ -1,0 +1,97 @@
+"""GPU parity of Phase-2 query attention and the LSE merge against the oracle
+(per-shard partials merged exactly; the merged output and log-sum-exp are
+compared), plus the merge kernel alone on random partials."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as OA
+from tests.gpu_cases import LSE_ABS, Case, assert_close, log, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_merged(case, seq, khat_cache=None):
+    w = case.w
+    if seq == 0:
+        if khat_cache is None:
+            khat = case.oracle_khat().astype(np.float64)
+            khat_cache = khat.reshape(w.n_blocks, w.block_size, w.n_kv_heads, w.head_dim).transpose(0, 2, 1, 3)
+        kc = khat_cache
+        vc = W.bf16_bits_to_f64(case.v).reshape(w.n_blocks, w.block_size, w.n_kv_heads, w.head_dim)
+        vc = vc.transpose(0, 2, 1, 3)
+    else:
+        kc = W.bf16_bits_to_f64(W.extra_cache(w, seq, "k"))
+        vc = W.bf16_bits_to_f64(W.extra_cache(w, seq, "v"))
+    qq = W.bf16_bits_to_f64(case.qq[seq])
+    ks = W.bf16_bits_to_f64(case.kq[seq]) if case.with_self else None
+    vs = W.bf16_bits_to_f64(case.vq[seq]) if case.with_self else None
+    parts = OA.phase2_partials(qq, w.context_len, kc, vc, ks, vs, w.rope_base)
+    return OA.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+
+
+def _compare(case, seqs):
+    o = case.path.o_q.cpu().numpy()
+    lse = case.path.lse_q.cpu().numpy()
+    for s in seqs:
+        want_o, want_lse = _oracle_merged(case, s)
+        assert_close(o[s], want_o, f"{case.w.name} phase2 merged O seq {s}")
+        assert_close(lse[s], want_lse, f"{case.w.name} phase2 merged LSE seq {s}",
+                     max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+SMALL = {
+    "tiny": {},
+    "ragged_shards": dict(n_blocks=3, block_size=1000, chunk_size=8, budget_chunks=15, n_planted=0,
+                          q_len=5),
+    "decode_batch": dict(n_blocks=5, block_size=512, q_len=1, batch=3, n_planted=0),
+    "g4_d128_lq64": dict(n_blocks=2, block_size=640, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                         q_len=64, budget_chunks=2, n_planted=0),
+    "g8_d128_lq40": dict(n_blocks=2, block_size=384, n_q_heads=8, n_kv_heads=1, head_dim=128,
+                         q_len=40, budget_chunks=2, n_planted=0),
+}
+
+
+@pytest.mark.parametrize("with_self", [True, False])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_phase2_small(name, with_self):
+    w = W.with_(W.CONFIGS["tiny"], name=name, **SMALL[name])
+    case = Case(w, with_self=with_self)
+    case.run()
+    _compare(case, range(w.batch))
+
+
+@pytest.mark.parametrize("name", ["32k", "128k"])
+def test_phase2_full_size(name):
+    w = W.CONFIGS[name]
+    case = Case(w)
+    case.run()
+    _compare(case, [0])
+
+
+def test_phase2_full_size_decode_batch():
+    w = W.CONFIGS["512k"]
+    case = Case(w)
+    case.run()
+    _compare(case, [0, 1, w.batch - 1])
+
+
+def test_merge_kernel_alone():
+    torch = torch_cuda()
+    from long_context_blockwise_max_amd import binding as B
+    rng = np.random.default_rng(3)
+    for (bsz, n_parts, lq, hq, d) in [(2, 7, 5, 4, 64), (1, 33, 64, 32, 128), (3, 1, 1, 8, 128)]:
+        o_part = rng.standard_normal((bsz, n_parts, lq, hq, d)).astype(np.float32)
+        lse_part = (rng.standard_normal((bsz, n_parts, lq, hq)) * 30).astype(np.float32)
+        if n_parts > 1:
+            lse_part[:, 0, 0, 0] = -np.inf       # an empty part contributes nothing
+        dev = torch.device("cuda")
+        op, lp = torch.from_numpy(o_part).to(dev), torch.from_numpy(lse_part).to(dev)
+        o = torch.empty((bsz, lq, hq, d), device=dev)
+        lse = torch.empty((bsz, lq, hq), device=dev)
+        log(f"[merge] B={bsz} parts={n_parts} Lq={lq} Hq={hq} d={d}")
+        B.pulsar_lse_merge(bsz, n_parts, lq, hq, d, op, lp, o, lse)
+        torch.cuda.synchronize()
+        want_o, want_lse = OA.lse_merge(np.moveaxis(o_part, 1, 0), np.moveaxis(lse_part, 1, 0))
+        assert_close(o.cpu().numpy(), want_o, "merge O", max_abs=1e-5, mean_abs=1e-6)
+        assert_close(lse.cpu().numpy(), want_lse, "merge LSE", max_abs=1e-4, mean_abs=1e-5)

@@ -18,6 +18,8 @@ place of text; Q/K/V are standard normal in place of model activations.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, replace
 
 import numpy as np
@@ -158,11 +160,35 @@ def qkv_block(w: Workload, which: str, j: int) -> np.ndarray:
     return _normal_bf16(rng, (w.block_size, _heads(w, which), w.head_dim))
 
 
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def qkv(w: Workload, which: str) -> np.ndarray:
-    """uint16 bf16 bits [L][H][d] of the whole context tensor."""
+    """uint16 bf16 bits [L][H][d] of the whole context tensor (blocks drawn in parallel)."""
     out = np.empty((w.context_len, _heads(w, which), w.head_dim), np.uint16)
-    for j in range(w.n_blocks):
+
+    def fill(j):
         out[j * w.block_size:(j + 1) * w.block_size] = qkv_block(w, which, j)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(w.n_blocks)))
+    return out
+
+
+def extra_cache(w: Workload, seq: int, which: str) -> np.ndarray:
+    """Whole retained cache [S][Hkv][b][d] of extra sequence `seq` (shards in parallel)."""
+    out = np.empty((w.n_blocks, w.n_kv_heads, w.block_size, w.head_dim), np.uint16)
+
+    def fill(s):
+        out[s] = extra_cache_shard(w, seq, which, s)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(w.n_blocks)))
     return out
 
 
