@@ -1,0 +1,204 @@
+"""Benchmark of the Pulsar Attention hot path on one MI355X.
+
+One step = the whole hot path over one synthetic context already resident in
+HBM: Max-IDF selection -> Phase-1 encoding (rotary cache fill + attention of
+every block over [sink || summaries || own block]) -> Phase-2 query attention
+over the retained shards and the query's own causal shard -> exact LSE merge.
+
+Default workload: 128K context as 8 blocks of 16K, Llama-3.1-8B attention
+geometry (32 query / 8 KV heads, head dim 128, bf16), sink 64, 2048-token
+summary budget per block, 64-token query.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Phase-1 TFLOP/s + Phase-2 KV GB/s (% roofline), Llama-3.1-8B attn @128K, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="128k", help="tiny | 32k | 128k | 128k_star | 512k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="oracle Phase-1 rows timed on the host")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, tok, q_bits, k_bits, v_bits, n_rows):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    Phase-1 rows of the last block (the longest prefix), all heads, including
+    the rotation of every key those rows see.  Returns a rate in TFLOP/s."""
+    import numpy as np
+
+    import workloads as W
+    from oracle import attention as OA
+    from oracle import selection as OS
+
+    t0 = time.perf_counter()
+    sel, _, _ = OS.select(tok, w.n_blocks, w.block_size, w.chunk_size, w.budget_chunks, w.vocab_size)
+    pre = OS.prefix_positions(sel, w.n_blocks, w.block_size, w.chunk_size, w.sink_size)
+    i = w.n_blocks - 1
+    rng = np.random.default_rng(0)
+    rows = sorted(int(r) for r in rng.choice(w.block_size, size=n_rows, replace=False))
+    r_max = max(rows)
+    keys = np.concatenate([pre[i], np.arange(i * w.block_size, i * w.block_size + r_max + 1)])
+    khat = np.zeros((w.context_len, w.n_kv_heads, w.head_dim), np.float32)
+    uk = np.unique(keys)
+    khat[uk] = OA.rotate_bf16(W.bf16_bits_to_f64(k_bits[uk]), uk, w.rope_base)
+
+    class Rows:
+        def __init__(self, bits):
+            self.bits = bits
+
+        def __getitem__(self, idx):
+            return W.bf16_bits_to_f64(self.bits[idx])
+
+    OA.phase1_rows(Rows(q_bits), khat, Rows(v_bits), pre, [(i, r) for r in rows], w.block_size,
+                   w.rope_base)
+    dt = time.perf_counter() - t0
+    flops = sum(4.0 * w.head_dim * w.n_q_heads * (len(pre[i]) + r + 1) for r in rows)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": (f"Phase-1 oracle (float64 numpy) on {n_rows} seeded rows of block {i} of the "
+                   f"{w.name} workload, all {w.n_q_heads} heads, incl. selection and key rotation; "
+                   f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s"),
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the hot path is one batched launch on a single "
+              "MI355X (every block of the context is a grid axis); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from long_context_blockwise_max_amd import costs as C
+    from long_context_blockwise_max_amd.pipeline import Geometry, HotPath
+
+    w = W.CONFIGS[args.config]
+    geo = Geometry(w.n_blocks, w.block_size, w.chunk_size, w.budget_chunks, w.sink_size,
+                   w.vocab_size, w.n_q_heads, w.n_kv_heads, w.head_dim, w.q_len, w.batch,
+                   w.rope_base, True)
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    tok = W.tokens(w)
+    q_bits, k_bits, v_bits = W.qkv(w, "q"), W.qkv(w, "k"), W.qkv(w, "v")
+    qq, kq, vq = W.query(w)
+    path = HotPath(geo, device="cuda")
+    path.upload(tok, q_bits, k_bits, v_bits, qq, kq, vq)
+    for s in range(1, w.batch):
+        path.upload_extra_cache(s, W.extra_cache(w, s, "k"), W.extra_cache(w, s, "v"))
+    torch.cuda.synchronize()
+    print("[bench] inputs resident; warming up", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        path.step()
+    torch.cuda.synchronize()
+
+    names = ("select", "phase1", "phase2", "merge")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        e = ev[k]
+        e[0].record(stream)
+        path.select()
+        e[1].record(stream)
+        path.phase1()
+        e[2].record(stream)
+        path.phase2()
+        e[3].record(stream)
+        path.merge()
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [] for n in names}
+    for e in ev:
+        for j, n in enumerate(names):
+            per[n].append(e[j].elapsed_time(e[j + 1]))
+    avg = {n: float(np.mean(per[n])) for n in names}
+    step_ms = wall * 1e3 / args.steps
+    print(f"[bench] per-call ms: {avg}", file=sys.stderr, flush=True)
+
+    p1_flops = C.phase1_flops_rows(w.n_blocks, w.block_size, w.sink_size, w.chunk_size, w.k_eff,
+                                   w.n_q_heads, w.head_dim)
+    p1_tflops = p1_flops / (avg["phase1"] * 1e-3) / 1e12
+    p2_bytes = C.phase2_bytes(w.batch, w.n_blocks, w.block_size, w.q_len, w.n_q_heads,
+                              w.n_kv_heads, w.head_dim, True)
+    p2_s = (avg["phase2"] + avg["merge"]) * 1e-3
+    p2_gbs = p2_bytes / p2_s / 1e9
+    p2_flops = C.phase2_flops(w.batch, w.q_len, w.context_len, w.n_q_heads, w.head_dim, True)
+    e2e_ms = sum(avg.values())
+    e2e_roof_ms = (p1_flops / (PEAK_BF16_TFLOPS * 1e12) + p2_bytes / (PEAK_HBM_GBS * 1e9)) * 1e3
+
+    out = {
+        "metric": METRIC,
+        "value": round(p1_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "context": w.context_len, "blocks": w.n_blocks,
+            "block_size": w.block_size, "sink": w.sink_size, "chunk": w.chunk_size,
+            "summary_tokens_per_block": w.k_eff * w.chunk_size, "q_heads": w.n_q_heads,
+            "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "query_tokens": w.q_len,
+            "batch": w.batch, "rope_base": w.rope_base,
+        },
+        "phase1": {"ms": round(avg["phase1"], 4), "tflops": round(p1_tflops, 2),
+                   "frac_bf16_peak": round(p1_tflops / PEAK_BF16_TFLOPS, 4),
+                   "algorithmic_flop": p1_flops},
+        "phase2": {"us": round((avg["phase2"] + avg["merge"]) * 1e3, 2),
+                   "query_us": round(avg["phase2"] * 1e3, 2), "merge_us": round(avg["merge"] * 1e3, 2),
+                   "kv_gbs": round(p2_gbs, 1), "frac_hbm_peak": round(p2_gbs / PEAK_HBM_GBS, 4),
+                   "algorithmic_bytes": p2_bytes,
+                   "tflops": round(p2_flops / p2_s / 1e12, 2)},
+        "select_us": round(avg["select"] * 1e3, 2),
+        "e2e_ms": round(e2e_ms, 4),
+        "e2e_frac_roofline": round(e2e_roof_ms / e2e_ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(p1_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(p1_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "pulsar_phase1_encode (rope_fill + phase1_kernel; events bracket the call)"},
+        "roofline_phase2": {"bound": "hbm", "achieved": round(p2_gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(p2_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cb = cpu_baseline(w, tok, q_bits, k_bits, v_bits, args.cpu_rows)
+        cb.pop("seconds")
+        cb["value"] = round(cb["value"], 6)
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

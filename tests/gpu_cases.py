@@ -84,11 +84,14 @@ class Case:
         return out
 
 
-def sample_rows(w: W.Workload, per_block_random=3, seed=0):
+def sample_rows(w: W.Workload, per_block_random=3, seed=0, sparse=False):
     """(block, row) pairs: the first and last rows, tile edges and a few seeded rows."""
     rng = np.random.default_rng(seed)
     b = w.block_size
-    fixed = sorted({0, 1, 31, 32, 63, 64, 127, 128, b // 2, b - 65, b - 64, b - 2, b - 1})
+    if sparse:
+        fixed = sorted({0, 63, 64, b - 1})
+    else:
+        fixed = sorted({0, 1, 31, 32, 63, 64, 127, 128, b // 2, b - 65, b - 64, b - 2, b - 1})
     fixed = [r for r in fixed if 0 <= r < b]
     rows = []
     for i in range(w.n_blocks):

@@ -102,5 +102,6 @@ def test_phase1_full_size_sampled(name):
     w = W.CONFIGS[name]
     case = Case(w, extra_seqs=False)
     case.run()
-    rows = sample_rows(w, per_block_random=2 if w.n_blocks > 8 else 3, seed=w.seed)
+    rows = sample_rows(w, per_block_random=1 if w.n_blocks > 8 else 3, seed=w.seed,
+                       sparse=w.n_blocks > 8)
     _sampled_compare(case, rows)
