@@ -49,12 +49,12 @@ extern "C" {
 
 /* Context geometry of one sequence.
  *   n_blocks      N >= 1 blocks ("hosts"), each of block_size tokens; L = N * block_size
- *   block_size    b, a multiple of chunk_size and of 64
- *   chunk_size    tokens per chunk; 32 is the method's value (the only one supported)
+ *   block_size    b, a multiple of chunk_size
+ *   chunk_size    tokens per chunk (32 is the method's value); a multiple of 8
  *   budget_chunks k chunks kept per block (12.5 % of b is k = b / 256); k >= n_chunks
  *                 keeps every chunk; 0 keeps none (Star Attention's anchor setting)
  *   sink_size     S first tokens of the sequence prepended to every block i > 0;
- *                 a multiple of chunk_size, 0 <= S <= L
+ *                 a multiple of 8, 0 <= S <= L
  *   vocab_size    V, token ids must lie in [0, V); V <= 1,048,576
  */
 typedef struct pulsar_geom {
@@ -66,7 +66,8 @@ typedef struct pulsar_geom {
   int32_t vocab_size;
 } pulsar_geom;
 
-/* Attention geometry.  head_dim 64 or 128; n_q_heads a multiple of n_kv_heads. */
+/* Attention geometry.  head_dim 64 or 128; n_q_heads = G * n_kv_heads with the
+ * group size G in {1, 2, 4} or a multiple of 8; L * n_kv_heads * head_dim < 2^31. */
 typedef struct pulsar_attn {
   int32_t n_q_heads;
   int32_t n_kv_heads;
@@ -76,7 +77,10 @@ typedef struct pulsar_attn {
 } pulsar_attn;
 
 /* Bytes of workspace pulsar_select and pulsar_phase1_encode need for this
- * geometry (one workspace serves both).  Returns 0 if the geometry is invalid. */
+ * geometry (one workspace serves both; a == NULL gives the smaller size that
+ * pulsar_select alone needs).  The Phase-1 part holds the rotated queries
+ * (L * Hq * d bf16), the prefix index lists and the work order.  Returns 0 if
+ * the geometry is invalid. */
 size_t pulsar_workspace_bytes(const pulsar_geom* g, const pulsar_attn* a);
 
 /* Number of chunks kept per block: min(budget_chunks, block_size / chunk_size). */
@@ -111,7 +115,8 @@ int pulsar_select(const pulsar_geom* g, const int32_t* tok, int32_t* sel,
  *   sel      [N][kept] int32 from pulsar_select (ascending within each block)
  *   o        [L][Hq][d] float32 out: attention output of every block row
  *   k_cache  [N][Hkv][b][d] bf16 out: RoPE(k) rounded to bf16
- *   v_cache  [N][Hkv][b][d] bf16 out: v
+ *   v_cache  [N][Hkv][d][b] bf16 out: v, stored d-major (each value row is a
+ *            column), so that the P.V contraction reads it in 16-byte runs
  *   ws       workspace (pulsar_workspace_bytes); ws_bytes its size
  * Errors: PULSAR_EINVAL, PULSAR_EWORKSPACE, PULSAR_EUNSUPPORTED, PULSAR_EHIP. */
 int pulsar_phase1_encode(const pulsar_geom* g, const pulsar_attn* a, const uint16_t* q,
@@ -125,6 +130,11 @@ int pulsar_phase1_encode(const pulsar_geom* g, const pulsar_attn* a, const uint1
 int32_t pulsar_phase2_num_parts(const pulsar_attn* a, int32_t batch, int32_t n_shards,
                                 int32_t shard_len, int32_t q_len, int32_t has_self);
 
+/* Bytes of workspace pulsar_phase2_query needs (rotated query, rotated self keys
+ * and a d-major copy of the self values).  Returns 0 on invalid arguments. */
+size_t pulsar_phase2_workspace_bytes(const pulsar_attn* a, int32_t batch, int32_t q_len,
+                                     int32_t has_self);
+
 /* Phase-2 query attention over retained shards ("Dropping the Anchor ..."
  * Section 2.2).  Query token t of sequence s sits at position q_pos0 + t.  For
  * every part (a contiguous key range of one shard, or the self shard) the call
@@ -133,17 +143,21 @@ int32_t pulsar_phase2_num_parts(const pulsar_attn* a, int32_t batch, int32_t n_s
  * the query tokens' own keys and values, attended causally (token t sees self
  * keys 0..t); pass k_self = v_self = NULL to attend to the retained shards only.
  *   qq               [B][Lq][Hq][d] bf16, pre-RoPE
- *   k_cache, v_cache [B][n_shards][Hkv][shard_len][d] bf16 (keys already rotated)
+ *   k_cache          [B][n_shards][Hkv][shard_len][d] bf16, keys already rotated
+ *   v_cache          [B][n_shards][Hkv][d][shard_len] bf16, d-major (the layout
+ *                    pulsar_phase1_encode writes); shard_len a multiple of 8
  *   k_self, v_self   [B][Lq][Hkv][d] bf16 pre-RoPE, or both NULL
  *   o_part           [B][n_parts][Lq][Hq][d] float32 out
  *   lse_part         [B][n_parts][Lq][Hq] float32 out
  *   n_parts          must equal pulsar_phase2_num_parts(...) for this shape
- * Errors: PULSAR_EINVAL, PULSAR_EUNSUPPORTED, PULSAR_EHIP. */
+ *   ws               workspace of pulsar_phase2_workspace_bytes(...) bytes
+ * Errors: PULSAR_EINVAL, PULSAR_EWORKSPACE, PULSAR_EUNSUPPORTED, PULSAR_EHIP. */
 int pulsar_phase2_query(const pulsar_attn* a, int32_t batch, int32_t n_shards,
                         int32_t shard_len, const uint16_t* qq, int32_t q_len,
                         int64_t q_pos0, const uint16_t* k_cache, const uint16_t* v_cache,
                         const uint16_t* k_self, const uint16_t* v_self, float* o_part,
-                        float* lse_part, int32_t n_parts, void* stream);
+                        float* lse_part, int32_t n_parts, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* Exact log-sum-exp merge of partial attention results (the Star Attention
  * review's corrected update: weight exp(s_h - s_global) on the normalised A_h):

@@ -22,7 +22,8 @@ PULSAR_EUNSUPPORTED = -4
 
 EXPORTED = (
     "pulsar_workspace_bytes", "pulsar_kept_chunks", "pulsar_select", "pulsar_phase1_encode",
-    "pulsar_phase2_num_parts", "pulsar_phase2_query", "pulsar_lse_merge", "pulsar_strerror",
+    "pulsar_phase2_num_parts", "pulsar_phase2_workspace_bytes", "pulsar_phase2_query",
+    "pulsar_lse_merge", "pulsar_strerror",
 )
 
 
@@ -66,8 +67,10 @@ def lib():
         L.pulsar_phase1_encode.restype = ctypes.c_int
         L.pulsar_phase2_num_parts.argtypes = [A, i32, i32, i32, i32, i32]
         L.pulsar_phase2_num_parts.restype = i32
+        L.pulsar_phase2_workspace_bytes.argtypes = [A, i32, i32, i32]
+        L.pulsar_phase2_workspace_bytes.restype = sz
         L.pulsar_phase2_query.argtypes = [A, i32, i32, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp,
-                                          i32, vp]
+                                          i32, vp, sz, vp]
         L.pulsar_phase2_query.restype = ctypes.c_int
         L.pulsar_lse_merge.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.pulsar_lse_merge.restype = ctypes.c_int
@@ -178,8 +181,13 @@ def pulsar_phase2_num_parts(attn: Attn, batch, n_shards, shard_len, q_len, has_s
     return n
 
 
+def pulsar_phase2_workspace_bytes(attn: Attn, batch, q_len, has_self) -> int:
+    return lib().pulsar_phase2_workspace_bytes(ctypes.byref(attn), batch, q_len,
+                                               1 if has_self else 0)
+
+
 def pulsar_phase2_query(attn: Attn, batch, n_shards, shard_len, qq, q_len, q_pos0, k_cache,
-                        v_cache, k_self, v_self, o_part, lse_part, n_parts, stream=None):
+                        v_cache, k_self, v_self, o_part, lse_part, n_parts, ws, stream=None):
     import torch
     hq, hkv, d = attn.n_q_heads, attn.n_kv_heads, attn.head_dim
     kv_n = batch * n_shards * hkv * shard_len * d
@@ -192,7 +200,7 @@ def pulsar_phase2_query(attn: Attn, batch, n_shards, shard_len, qq, q_len, q_pos
         _bf16(k_self, self_n, "k_self", allow_none=True),
         _bf16(v_self, self_n, "v_self", allow_none=True),
         _ptr(o_part, torch.float32, rows * d, "o_part"), _ptr(lse_part, torch.float32, rows, "lse_part"),
-        n_parts, _stream(stream))
+        n_parts, _ptr(ws, torch.uint8, 0, "ws"), ws.numel(), _stream(stream))
     _check(rc, "pulsar_phase2_query")
 
 

@@ -29,6 +29,8 @@ int check_geom(const pulsar_geom* g) {
       g->sink_size < 0 || g->vocab_size < 1)
     return PULSAR_EINVAL;
   if (g->block_size % g->chunk_size != 0) return PULSAR_EINVAL;
+  // the d-major value tiles move keys in runs of 8: runs must not straddle a chunk or the sink
+  if (g->chunk_size % 8 != 0 || g->sink_size % 8 != 0) return PULSAR_EUNSUPPORTED;
   const int64_t L = (int64_t)g->n_blocks * g->block_size;
   if (L > kMaxContext) return PULSAR_EUNSUPPORTED;
   if (g->vocab_size > kMaxVocab) return PULSAR_EUNSUPPORTED;
@@ -48,12 +50,20 @@ int check_attn(const pulsar_attn* a) {
   if (!(a->rope_base > 1.0) || !isfinite(a->rope_base)) return PULSAR_EINVAL;
   if (a->head_dim != 64 && a->head_dim != 128) return PULSAR_EUNSUPPORTED;
   const int group = a->n_q_heads / a->n_kv_heads;
-  if (!(group == 1 || group == 2 || group % 4 == 0)) return PULSAR_EUNSUPPORTED;
+  if (!(group == 1 || group == 2 || group == 4 || group % 8 == 0)) return PULSAR_EUNSUPPORTED;
   return PULSAR_OK;
 }
 
+// cache element offsets are formed in 32-bit list entries: L * Hkv * d must fit
+int check_pair(const pulsar_geom* g, const pulsar_attn* a) {
+  const int64_t L = (int64_t)g->n_blocks * g->block_size;
+  if (L * a->n_kv_heads * a->head_dim > INT32_MAX) return PULSAR_EUNSUPPORTED;
+  return PULSAR_OK;
+}
+
+// select + phase 1 workspace: status word | df | rotated q | prefix lists | work order
 struct Layout {
-  size_t status, df, rope, order, total;
+  size_t status, df, q_rot, lists, order, total;
 };
 
 Layout layout(const pulsar_geom* g, const pulsar_attn* a) {
@@ -64,14 +74,38 @@ Layout layout(const pulsar_geom* g, const pulsar_attn* a) {
   l.df = off;
   off = align_up(off + (size_t)g->vocab_size * 4);
   const int64_t L = (int64_t)g->n_blocks * g->block_size;
-  l.rope = off;
-  if (a) off = align_up(off + (size_t)L * (a->head_dim / 2) * 8);
-  l.order = off;
+  l.q_rot = l.lists = l.order = off;
   if (a) {
     Phase1Geometry pg = phase1_geometry(g->n_blocks, g->block_size, g->chunk_size,
                                         kept_chunks(g), g->sink_size, a->n_q_heads,
                                         a->n_kv_heads, a->head_dim);
+    l.q_rot = off;
+    off = align_up(off + (size_t)L * a->n_q_heads * a->head_dim * 2);
+    l.lists = off;
+    off = align_up(off + (size_t)phase1_prefix_total(pg) * 2 * 4);
+    l.order = off;
     off = align_up(off + (size_t)pg.n_blocks * pg.n_row_tiles * 4);
+  }
+  l.total = off;
+  return l;
+}
+
+// phase 2 workspace: rotated query | rotated self keys | d-major self values
+struct Layout2 {
+  size_t q_rot, k_rot, v_t, total;
+};
+
+Layout2 layout2(const Phase2Geometry& pg) {
+  Layout2 l{};
+  size_t off = 0;
+  const size_t tok = (size_t)pg.batch * pg.q_len;
+  l.q_rot = off;
+  off = align_up(off + tok * pg.n_q_heads * pg.head_dim * 2);
+  l.k_rot = l.v_t = off;
+  if (pg.has_self) {
+    off = align_up(off + tok * pg.n_kv_heads * pg.head_dim * 2);
+    l.v_t = off;
+    off = align_up(off + (size_t)pg.batch * pg.n_kv_heads * pg.head_dim * pg.self_pad * 2);
   }
   l.total = off;
   return l;
@@ -85,7 +119,7 @@ extern "C" {
 
 size_t pulsar_workspace_bytes(const pulsar_geom* g, const pulsar_attn* a) {
   if (check_geom(g) != PULSAR_OK) return 0;
-  if (a && check_attn(a) != PULSAR_OK) return 0;
+  if (a && (check_attn(a) != PULSAR_OK || check_pair(g, a) != PULSAR_OK)) return 0;
   return layout(g, a).total;
 }
 
@@ -123,6 +157,8 @@ int pulsar_phase1_encode(const pulsar_geom* g, const pulsar_attn* a, const uint1
   if (rc) return rc;
   rc = check_attn(a);
   if (rc) return rc;
+  rc = check_pair(g, a);
+  if (rc) return rc;
   const int32_t kept = kept_chunks(g);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(k_cache) ||
       !aligned16(v_cache))
@@ -132,16 +168,17 @@ int pulsar_phase1_encode(const pulsar_geom* g, const pulsar_attn* a, const uint1
   if (!ws || ws_bytes < l.total) return PULSAR_EWORKSPACE;
   if (!aligned16(ws)) return PULSAR_EINVAL;
   char* w = static_cast<char*>(ws);
-  float* rope_cs = reinterpret_cast<float*>(w + l.rope);
+  uint16_t* q_rot = reinterpret_cast<uint16_t*>(w + l.q_rot);
+  int32_t* lists = reinterpret_cast<int32_t*>(w + l.lists);
   int32_t* order = reinterpret_cast<int32_t*>(w + l.order);
   const int64_t L = (int64_t)g->n_blocks * g->block_size;
   hipStream_t s = as_stream(stream);
-  if (launch_rope_fill(k, v, L, g->block_size, a->n_kv_heads, a->head_dim, a->rope_base, rope_cs,
-                       k_cache, v_cache, s))
+  if (launch_rope_fill(q, k, v, L, g->block_size, a->n_q_heads, a->n_kv_heads, a->head_dim,
+                       a->rope_base, q_rot, k_cache, v_cache, s))
     return PULSAR_EHIP;
   Phase1Geometry pg = phase1_geometry(g->n_blocks, g->block_size, g->chunk_size, kept,
                                       g->sink_size, a->n_q_heads, a->n_kv_heads, a->head_dim);
-  if (launch_phase1(pg, q, k_cache, v_cache, sel, rope_cs, order, o, s)) return PULSAR_EHIP;
+  if (launch_phase1(pg, q_rot, k_cache, v_cache, sel, lists, order, o, s)) return PULSAR_EHIP;
   return PULSAR_OK;
 }
 
@@ -156,11 +193,19 @@ int32_t pulsar_phase2_num_parts(const pulsar_attn* a, int32_t batch, int32_t n_s
   return pg.n_parts;
 }
 
+size_t pulsar_phase2_workspace_bytes(const pulsar_attn* a, int32_t batch, int32_t q_len,
+                                     int32_t has_self) {
+  if (check_attn(a) != PULSAR_OK || batch < 1 || q_len < 1) return 0;
+  Phase2Geometry pg = phase2_geometry(batch, 1, 1, q_len, a->n_q_heads, a->n_kv_heads,
+                                      a->head_dim, has_self);
+  return layout2(pg).total;
+}
+
 int pulsar_phase2_query(const pulsar_attn* a, int32_t batch, int32_t n_shards, int32_t shard_len,
                         const uint16_t* qq, int32_t q_len, int64_t q_pos0,
                         const uint16_t* k_cache, const uint16_t* v_cache, const uint16_t* k_self,
                         const uint16_t* v_self, float* o_part, float* lse_part, int32_t n_parts,
-                        void* stream) {
+                        void* ws, size_t ws_bytes, void* stream) {
   const int has_self = k_self != nullptr || v_self != nullptr;
   const int32_t want = pulsar_phase2_num_parts(a, batch, n_shards, shard_len, q_len, has_self);
   if (want <= 0) return want < 0 ? want : PULSAR_EINVAL;
@@ -168,11 +213,29 @@ int pulsar_phase2_query(const pulsar_attn* a, int32_t batch, int32_t n_shards, i
   if (has_self && (!aligned16(k_self) || !aligned16(v_self))) return PULSAR_EINVAL;
   if (!aligned16(qq) || !aligned16(o_part) || !lse_part) return PULSAR_EINVAL;
   if (n_shards > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) return PULSAR_EINVAL;
+  if (n_shards > 0 && shard_len % 8 != 0) return PULSAR_EUNSUPPORTED;  // d-major value runs of 8
   if (q_pos0 < 0) return PULSAR_EINVAL;
+  if ((int64_t)batch * n_shards * shard_len * a->n_kv_heads > INT32_MAX) return PULSAR_EUNSUPPORTED;
   Phase2Geometry pg = phase2_geometry(batch, n_shards, n_shards > 0 ? shard_len : 1, q_len,
                                       a->n_q_heads, a->n_kv_heads, a->head_dim, has_self);
-  return launch_phase2(pg, qq, q_pos0, k_cache, v_cache, k_self, v_self, a->rope_base, o_part,
-                       lse_part, as_stream(stream)) == 0
+  const Layout2 l = layout2(pg);
+  if (!ws || ws_bytes < l.total) return PULSAR_EWORKSPACE;
+  if (!aligned16(ws)) return PULSAR_EINVAL;
+  char* w = static_cast<char*>(ws);
+  uint16_t* q_rot = reinterpret_cast<uint16_t*>(w + l.q_rot);
+  uint16_t* k_rot = has_self ? reinterpret_cast<uint16_t*>(w + l.k_rot) : nullptr;
+  uint16_t* v_t = has_self ? reinterpret_cast<uint16_t*>(w + l.v_t) : nullptr;
+  hipStream_t s = as_stream(stream);
+  const int64_t tok = (int64_t)batch * q_len;
+  if (launch_rope_rows(qq, q_rot, tok, a->n_q_heads, a->head_dim, q_pos0, q_len, a->rope_base, s))
+    return PULSAR_EHIP;
+  if (has_self) {
+    if (launch_rope_rows(k_self, k_rot, tok, a->n_kv_heads, a->head_dim, q_pos0, q_len,
+                         a->rope_base, s) ||
+        launch_v_self_fill(v_self, batch, q_len, pg.self_pad, a->n_kv_heads, a->head_dim, v_t, s))
+      return PULSAR_EHIP;
+  }
+  return launch_phase2(pg, q_rot, k_cache, v_cache, k_rot, v_t, o_part, lse_part, s) == 0
              ? PULSAR_OK
              : PULSAR_EHIP;
 }

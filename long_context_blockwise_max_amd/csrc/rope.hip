@@ -1,73 +1,163 @@
-// Rotary table and retained-cache fill (HBM-bound elementwise passes).
+// Rotary embedding and retained-cache fill (HBM-bound elementwise passes).
 //
 // Every token keeps its original position ID ("Dropping the Anchor ..."
 // Section 2.1; the Star Attention review notes the anchor keeps its original
 // indices).  Rotation is the rotate-half form: the pair (x_i, x_{i+d/2}) is
 // turned by theta = pos * base^(-2i/d).  theta, cos and sin are float64 and
 // rounded to float32 once; at positions near 5e5 a float32 product
-// pos * inv_freq would already be off by up to ~0.03 rad.
+// pos * inv_freq would already be off by up to ~0.03 rad.  The rotated values
+// are rounded to bf16: they are the attention kernels' MFMA operands.
 //
-//   rope_table   cos/sin [L][d/2] float2, read by the Phase-1 query loader
-//   rope_fill    k_cache = bf16(RoPE(k)), v_cache = v, re-laid out from
-//                [L][Hkv][d] to the per-block, per-head [N][Hkv][b][d]
-//                (the KV each block keeps after Phase 1)
+//   rope_fill    Phase-1 prep: q_rot = bf16(RoPE(q)); k_cache = bf16(RoPE(k))
+//                re-laid out from [L][Hkv][d] to the per-block, per-head
+//                [N][Hkv][b][d] (the keys each block keeps)
+//   v_cache_fill the values each block keeps, d-major: [N][Hkv][d][b]
+//   rope_rows    Phase-2 prep: rotate query-host rows [T][H][d] at positions
+//                pos0 + (t % tok_per_seq)
+//
+// One thread per (token, 8-wide pair chunk c): it derives cos/sin for the 8
+// frequencies 8c .. 8c+7 once and applies them to elements [8c, 8c+8) and
+// [d/2 + 8c, d/2 + 8c + 8) of every head of the token.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace pulsar {
 
-__global__ void __launch_bounds__(256) rope_table(float2* __restrict__ cs, int64_t L, int half,
-                                                  double base) {
-  const int64_t n = L * half;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    int64_t pos = idx / half;
-    int i = (int)(idx - pos * half);
-    float c, s;
-    rope_cos_sin(pos, i, half, base, &c, &s);
-    cs[idx] = make_float2(c, s);
-  }
+template <int D>
+__device__ __forceinline__ void chunk_angles(int64_t pos, int c, double base, float (&cs)[8],
+                                             float (&sn)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) rope_cos_sin(pos, 8 * c + e, D / 2, base, &cs[e], &sn[e]);
 }
 
-// One thread per (position, kv head, 8-wide pair chunk): loads elements
-// [8c, 8c+8) and [d/2 + 8c, d/2 + 8c + 8) of a key row and of a value row.
 template <int D>
-__global__ void __launch_bounds__(256) rope_fill(const uint16_t* __restrict__ k,
-                                                 const uint16_t* __restrict__ v,
-                                                 const float2* __restrict__ cs, int64_t L,
-                                                 int32_t block_size, int32_t n_kv,
-                                                 uint16_t* __restrict__ kc,
-                                                 uint16_t* __restrict__ vc) {
+__device__ __forceinline__ void rotate_chunk(const uint16_t* src, uint16_t* dst, int c,
+                                             const float (&cs)[8], const float (&sn)[8]) {
+  constexpr int HALF = D / 2;
+  const u32x4 x1 = *(const u32x4*)(src + 8 * c);
+  const u32x4 x2 = *(const u32x4*)(src + HALF + 8 * c);
+  u32x4 y1, y2;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a0 = bf16_to_f32(x1[e] & 0xffffu), a1 = bf16_to_f32(x1[e] >> 16);
+    const float b0 = bf16_to_f32(x2[e] & 0xffffu), b1 = bf16_to_f32(x2[e] >> 16);
+    const float c0 = cs[2 * e], c1 = cs[2 * e + 1], s0 = sn[2 * e], s1 = sn[2 * e + 1];
+    y1[e] = pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+    y2[e] = pack_bf16x2(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+  }
+  *(u32x4*)(dst + 8 * c) = y1;
+  *(u32x4*)(dst + HALF + 8 * c) = y2;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) rope_fill(const uint16_t* __restrict__ q,
+                                                 const uint16_t* __restrict__ k, int64_t L,
+                                                 int32_t block_size, int32_t n_q, int32_t n_kv,
+                                                 double base, uint16_t* __restrict__ q_rot,
+                                                 uint16_t* __restrict__ kc) {
   constexpr int HALF = D / 2;
   constexpr int CPH = HALF / 8;  // pair chunks per head row
-  const int64_t n = L * n_kv * CPH;
+  const int64_t n = L * CPH;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int c = (int)(idx % CPH);
-    const int64_t rest = idx / CPH;
-    const int hd = (int)(rest % n_kv);
-    const int64_t pos = rest / n_kv;
-    const int64_t src = (pos * n_kv + hd) * D;
+    const int64_t pos = idx / CPH;
+    float cs[8], sn[8];
+    chunk_angles<D>(pos, c, base, cs, sn);
+    for (int h = 0; h < n_q; ++h) {
+      const int64_t r = (pos * n_q + h) * D;
+      rotate_chunk<D>(q + r, q_rot + r, c, cs, sn);
+    }
     const int64_t blk = pos / block_size;
     const int64_t w = pos - blk * block_size;
-    const int64_t dst = ((blk * n_kv + hd) * block_size + w) * D;
-    const u32x4 x1 = *(const u32x4*)(k + src + 8 * c);
-    const u32x4 x2 = *(const u32x4*)(k + src + HALF + 8 * c);
-    const float2* csr = cs + pos * HALF + 8 * c;
-    u32x4 y1, y2;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float2 cs0 = csr[2 * e], cs1 = csr[2 * e + 1];
-      const float a0 = bf16_to_f32(x1[e] & 0xffffu), a1 = bf16_to_f32(x1[e] >> 16);
-      const float b0 = bf16_to_f32(x2[e] & 0xffffu), b1 = bf16_to_f32(x2[e] >> 16);
-      y1[e] = pack_bf16x2(a0 * cs0.x - b0 * cs0.y, a1 * cs1.x - b1 * cs1.y);
-      y2[e] = pack_bf16x2(b0 * cs0.x + a0 * cs0.y, b1 * cs1.x + a1 * cs1.y);
+    for (int h = 0; h < n_kv; ++h) {
+      const int64_t src = (pos * n_kv + h) * D;
+      const int64_t dst = ((blk * n_kv + h) * block_size + w) * D;
+      rotate_chunk<D>(k + src, kc + dst, c, cs, sn);
     }
-    *(u32x4*)(kc + dst + 8 * c) = y1;
-    *(u32x4*)(kc + dst + HALF + 8 * c) = y2;
-    *(u32x4*)(vc + dst + 8 * c) = *(const u32x4*)(v + src + 8 * c);
-    *(u32x4*)(vc + dst + HALF + 8 * c) = *(const u32x4*)(v + src + HALF + 8 * c);
   }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) rope_rows(const uint16_t* __restrict__ x,
+                                                 uint16_t* __restrict__ y, int64_t n_tok,
+                                                 int32_t heads, int64_t pos0, int32_t tok_per_seq,
+                                                 double base) {
+  constexpr int CPH = D / 16;
+  const int64_t n = n_tok * CPH;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(idx % CPH);
+    const int64_t t = idx / CPH;
+    float cs[8], sn[8];
+    chunk_angles<D>(pos0 + t % tok_per_seq, c, base, cs, sn);
+    for (int h = 0; h < heads; ++h) {
+      const int64_t r = (t * heads + h) * D;
+      rotate_chunk<D>(x + r, y + r, c, cs, sn);
+    }
+  }
+}
+
+// d-major V: v [T][Hkv][D] -> vt, element (t, h, d) at vt_index(t, h) + d * ld.
+// One workgroup transposes 64 tokens x D of one head through LDS; every thread
+// then writes 16-byte runs of 8 consecutive tokens of one d-row.  The 8 tokens
+// of a run never straddle a block (tokens are grouped from a multiple of 64
+// and the block length is a multiple of 8).
+template <int D, class Dst>
+__device__ __forceinline__ void transpose_tile(const uint16_t* __restrict__ v, int64_t n_tok,
+                                               int32_t n_kv, Dst dst) {
+  __shared__ uint16_t tile[64][D + 8];
+  const int h = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  constexpr int CPR = D / 8;
+  for (int idx = threadIdx.x; idx < 64 * CPR; idx += blockDim.x) {
+    const int r = idx / CPR, c = idx % CPR;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (t0 + r < n_tok) x = *(const u32x4*)(v + ((t0 + r) * n_kv + h) * D + 8 * c);
+    *(u32x4*)(&tile[r][8 * c]) = x;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < D * 8; idx += blockDim.x) {
+    const int d = idx / 8, run = idx % 8;
+    const int64_t t = t0 + 8 * run;
+    if (t >= n_tok) continue;
+    u32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      y[e] = (uint32_t)tile[8 * run + 2 * e][d] | ((uint32_t)tile[8 * run + 2 * e + 1][d] << 16);
+    *(u32x4*)(dst(t, h, d)) = y;
+  }
+}
+
+// retained V cache: [N][Hkv][D][b]
+template <int D>
+__global__ void __launch_bounds__(256) v_cache_fill(const uint16_t* __restrict__ v, int64_t L,
+                                                    int32_t block_size, int32_t n_kv,
+                                                    uint16_t* __restrict__ vc) {
+  transpose_tile<D>(v, L, n_kv, [&](int64_t t, int h, int d) {
+    const int64_t blk = t / block_size, w = t - blk * block_size;
+    return vc + ((blk * n_kv + h) * D + d) * block_size + w;
+  });
+}
+
+// query-host values [B][Lq][Hkv][D] -> [B][Hkv][D][lq_pad], zero past Lq
+template <int D>
+__global__ void __launch_bounds__(256) v_self_fill(const uint16_t* __restrict__ v, int32_t lq,
+                                                   int32_t lq_pad, int32_t n_kv,
+                                                   uint16_t* __restrict__ vt) {
+  const int bb = blockIdx.z;
+  const uint16_t* src = v + (int64_t)bb * lq * n_kv * D;
+  uint16_t* base = vt + (int64_t)bb * n_kv * D * lq_pad;
+  transpose_tile<D>(src, lq, n_kv, [&](int64_t t, int h, int d) {
+    return base + ((int64_t)h * D + d) * lq_pad + t;
+  });
+  // zero the padding columns [lq, lq_pad) of this workgroup's head
+  const int h = blockIdx.y;
+  if (blockIdx.x == 0)
+    for (int idx = threadIdx.x; idx < D * (lq_pad - lq); idx += blockDim.x) {
+      const int d = idx / (lq_pad - lq), t = lq + idx % (lq_pad - lq);
+      base[((int64_t)h * D + d) * lq_pad + t] = 0;
+    }
 }
 
 static int grid_for(int64_t n, int threads) {
@@ -77,20 +167,46 @@ static int grid_for(int64_t n, int threads) {
   return (int)g;
 }
 
-int launch_rope_fill(const uint16_t* k, const uint16_t* v, int64_t L, int32_t block_size,
-                     int32_t n_kv_heads, int32_t head_dim, double rope_base, float* rope_cs,
-                     uint16_t* k_cache, uint16_t* v_cache, hipStream_t stream) {
-  const int half = head_dim / 2;
-  float2* cs = reinterpret_cast<float2*>(rope_cs);
-  hipLaunchKernelGGL(rope_table, dim3(grid_for(L * half, 256)), dim3(256), 0, stream, cs, L, half,
-                     rope_base);
-  const int64_t n = L * n_kv_heads * (half / 8);
+int launch_rope_fill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t L,
+                     int32_t block_size, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                     double rope_base, uint16_t* q_rot, uint16_t* k_cache, uint16_t* v_cache,
+                     hipStream_t stream) {
+  const int64_t n = L * (head_dim / 16);
+  const dim3 tgrid((unsigned)((L + 63) / 64), (unsigned)n_kv_heads);
+  if (head_dim == 128) {
+    hipLaunchKernelGGL(rope_fill<128>, dim3(grid_for(n, 256)), dim3(256), 0, stream, q, k, L,
+                       block_size, n_q_heads, n_kv_heads, rope_base, q_rot, k_cache);
+    hipLaunchKernelGGL(v_cache_fill<128>, tgrid, dim3(256), 0, stream, v, L, block_size,
+                       n_kv_heads, v_cache);
+  } else {
+    hipLaunchKernelGGL(rope_fill<64>, dim3(grid_for(n, 256)), dim3(256), 0, stream, q, k, L,
+                       block_size, n_q_heads, n_kv_heads, rope_base, q_rot, k_cache);
+    hipLaunchKernelGGL(v_cache_fill<64>, tgrid, dim3(256), 0, stream, v, L, block_size,
+                       n_kv_heads, v_cache);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int launch_v_self_fill(const uint16_t* v, int32_t batch, int32_t q_len, int32_t lq_pad,
+                       int32_t n_kv_heads, int32_t head_dim, uint16_t* vt, hipStream_t stream) {
+  const dim3 grid((unsigned)((q_len + 63) / 64), (unsigned)n_kv_heads, (unsigned)batch);
   if (head_dim == 128)
-    hipLaunchKernelGGL(rope_fill<128>, dim3(grid_for(n, 256)), dim3(256), 0, stream, k, v, cs, L,
-                       block_size, n_kv_heads, k_cache, v_cache);
+    hipLaunchKernelGGL(v_self_fill<128>, grid, dim3(256), 0, stream, v, q_len, lq_pad, n_kv_heads, vt);
   else
-    hipLaunchKernelGGL(rope_fill<64>, dim3(grid_for(n, 256)), dim3(256), 0, stream, k, v, cs, L,
-                       block_size, n_kv_heads, k_cache, v_cache);
+    hipLaunchKernelGGL(v_self_fill<64>, grid, dim3(256), 0, stream, v, q_len, lq_pad, n_kv_heads, vt);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int launch_rope_rows(const uint16_t* x, uint16_t* y, int64_t n_tok, int32_t heads,
+                     int32_t head_dim, int64_t pos0, int32_t tok_per_seq, double rope_base,
+                     hipStream_t stream) {
+  const int64_t n = n_tok * (head_dim / 16);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(rope_rows<128>, dim3(grid_for(n, 256)), dim3(256), 0, stream, x, y, n_tok,
+                       heads, pos0, tok_per_seq, rope_base);
+  else
+    hipLaunchKernelGGL(rope_rows<64>, dim3(grid_for(n, 256)), dim3(256), 0, stream, x, y, n_tok,
+                       heads, pos0, tok_per_seq, rope_base);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -71,7 +71,8 @@ class HotPath:
         self.v = _bf16_empty((L, hkv, d), dev)
         self.o = torch.empty((L, hq, d), dtype=torch.float32, device=dev)
         self.k_cache = _bf16_empty((g.batch, g.n_blocks, hkv, g.block_size, d), dev)
-        self.v_cache = _bf16_empty((g.batch, g.n_blocks, hkv, g.block_size, d), dev)
+        # retained values are d-major: [B][N][Hkv][d][b]
+        self.v_cache = _bf16_empty((g.batch, g.n_blocks, hkv, d, g.block_size), dev)
         self.qq = _bf16_empty((g.batch, g.q_len, hq, d), dev)
         self.k_self = _bf16_empty((g.batch, g.q_len, hkv, d), dev) if g.with_self else None
         self.v_self = _bf16_empty((g.batch, g.q_len, hkv, d), dev) if g.with_self else None
@@ -81,6 +82,9 @@ class HotPath:
                                   device=dev)
         self.lse_part = torch.empty((g.batch, self.n_parts, g.q_len, hq), dtype=torch.float32,
                                     device=dev)
+        self.ws2 = torch.empty(B.pulsar_phase2_workspace_bytes(self.cattn, g.batch, g.q_len,
+                                                               g.with_self),
+                               dtype=torch.uint8, device=dev)
         self.o_q = torch.empty((g.batch, g.q_len, hq, d), dtype=torch.float32, device=dev)
         self.lse_q = torch.empty((g.batch, g.q_len, hq), dtype=torch.float32, device=dev)
 
@@ -100,8 +104,11 @@ class HotPath:
                 self._bits_to_dev(dst, src)
 
     def upload_extra_cache(self, seq, k_bits, v_bits):
+        """Retained cache of another sequence: k_bits, v_bits [N][Hkv][b][d] bf16 bits
+        (values are transposed to the d-major layout on the device)."""
         self._bits_to_dev(self.k_cache[seq], k_bits)
-        self._bits_to_dev(self.v_cache[seq], v_bits)
+        t = torch.from_numpy(v_bits.view("int16")).view(torch.bfloat16).to(self.device)
+        self.v_cache[seq].copy_(t.transpose(-1, -2))
 
     # the four calls -------------------------------------------------------
     def select(self, stream=None):
@@ -117,7 +124,7 @@ class HotPath:
         g = self.geo
         B.pulsar_phase2_query(self.cattn, g.batch, g.n_blocks, g.block_size, self.qq, g.q_len,
                               g.context_len, self.k_cache, self.v_cache, self.k_self, self.v_self,
-                              self.o_part, self.lse_part, self.n_parts, stream)
+                              self.o_part, self.lse_part, self.n_parts, self.ws2, stream)
 
     def merge(self, stream=None):
         g = self.geo

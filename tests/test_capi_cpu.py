@@ -54,9 +54,11 @@ def test_workspace_and_kept_chunks():
     ws_sel = B.pulsar_workspace_bytes(g, None)
     ws_all = B.pulsar_workspace_bytes(g, ATTN)
     assert ws_sel >= 128256 * 4
-    # rotary table (L x d/2 float2) + work order fit in the full workspace
-    assert ws_all >= ws_sel + 131072 * 64 * 8
+    # rotated queries (L x Hq x d bf16) + prefix lists + work order
+    assert ws_all >= ws_sel + 131072 * 32 * 128 * 2
     assert B.pulsar_workspace_bytes(geom(block_size=100), ATTN) == 0    # not a chunk multiple
+    assert B.pulsar_workspace_bytes(geom(chunk_size=12, block_size=1200), ATTN) == 0  # chunk % 8
+    assert B.pulsar_workspace_bytes(geom(sink_size=60), ATTN) == 0     # sink % 8
     assert B.pulsar_workspace_bytes(g, B.make_attn(32, 8, 96, 5e5)) == 0   # head_dim
     assert B.pulsar_workspace_bytes(g, B.make_attn(30, 8, 128, 5e5)) == 0  # Hq % Hkv
 
@@ -121,15 +123,24 @@ def test_phase2_part_count_and_rejections():
     lib = B.lib()
     with pytest.raises(B.PulsarError):
         B.pulsar_phase2_num_parts(ATTN, 0, 8, 16384, 64, True)
-    rc = lib.pulsar_phase2_query(ctypes.byref(ATTN), 1, 8, 16384, FAKE, 64, 131072, FAKE, FAKE,
-                                 FAKE, FAKE, FAKE, FAKE, n + 1, None)
-    assert rc == B.PULSAR_EINVAL                      # wrong part count
-    rc = lib.pulsar_phase2_query(ctypes.byref(ATTN), 1, 8, 16384, FAKE, 64, 131072, FAKE, FAKE,
-                                 FAKE, None, FAKE, FAKE, n, None)
-    assert rc == B.PULSAR_EINVAL                      # k_self without v_self
-    rc = lib.pulsar_phase2_query(ctypes.byref(ATTN), 1, 8, 16384, FAKE, 64, -1, FAKE, FAKE,
-                                 FAKE, FAKE, FAKE, FAKE, n, None)
-    assert rc == B.PULSAR_EINVAL                      # negative position
+    ws2 = B.pulsar_phase2_workspace_bytes(ATTN, 1, 64, True)
+    assert ws2 >= 64 * (32 + 8) * 128 * 2
+    assert B.pulsar_phase2_workspace_bytes(ATTN, 1, 64, False) < ws2
+
+    def q2(*args):
+        return lib.pulsar_phase2_query(ctypes.byref(ATTN), *args)
+
+    assert q2(1, 8, 16384, FAKE, 64, 131072, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n + 1, FAKE, ws2,
+              None) == B.PULSAR_EINVAL                # wrong part count
+    assert q2(1, 8, 16384, FAKE, 64, 131072, FAKE, FAKE, FAKE, None, FAKE, FAKE, n, FAKE, ws2,
+              None) == B.PULSAR_EINVAL                # k_self without v_self
+    assert q2(1, 8, 16384, FAKE, 64, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, FAKE, ws2,
+              None) == B.PULSAR_EINVAL                # negative position
+    assert q2(1, 8, 16384, FAKE, 64, 131072, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, FAKE, ws2 - 1,
+              None) == B.PULSAR_EWORKSPACE
+    n_odd = B.pulsar_phase2_num_parts(ATTN, 1, 8, 1001, 64, True)
+    assert q2(1, 8, 1001, FAKE, 64, 131072, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n_odd, FAKE, ws2,
+              None) == B.PULSAR_EUNSUPPORTED          # shard length not a multiple of 8
 
 
 @needs_lib

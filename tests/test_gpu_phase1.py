@@ -21,7 +21,8 @@ def _cache_check(case):
     w = case.w
     kc = case.path.k_cache[0].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
     vc = case.path.v_cache[0].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
-    want_v = case.v.reshape(w.n_blocks, w.block_size, w.n_kv_heads, w.head_dim).transpose(0, 2, 1, 3)
+    # retained values are stored d-major: [N][Hkv][d][b]
+    want_v = case.v.reshape(w.n_blocks, w.block_size, w.n_kv_heads, w.head_dim).transpose(0, 2, 3, 1)
     np.testing.assert_array_equal(vc, want_v)
     khat = case.oracle_khat().reshape(w.n_blocks, w.block_size, w.n_kv_heads, w.head_dim)
     khat = khat.transpose(0, 2, 1, 3)
