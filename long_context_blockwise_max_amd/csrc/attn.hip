@@ -110,13 +110,13 @@ __device__ __forceinline__ void flash_init(FlashState<D, NQ>& st) {
 // hold without loss, and O / l at the end is the same ratio either way.
 constexpr float kRescaleSlack = 8.f;
 
-// One 32-key subtile `kt` (0 or 1) of the staged tile.  valid(key, qt) is
-// consulted only when MASK: it tells whether subtile key `key` (0..31) is
-// visible to this lane's query row of query subtile qt.
-template <int D, int NQ, bool MASK, class Valid>
+// One 32-key subtile `kt` (0 or 1) of the staged tile.  Keys 0 .. lim-1 of the
+// subtile are visible to this lane's query row (lim >= 32: all of them); the
+// mask is applied only when some lane of the wave needs it.
+template <int D, int NQ>
 __device__ __forceinline__ void flash_sub(const char* stage, int kt,
                                           const bf16x8 (&q)[NQ][D / 16],
-                                          FlashState<D, NQ>& st, float sl2, Valid valid) {
+                                          FlashState<D, NQ>& st, float sl2, int lim) {
   using KTl = KTile<D>;
   using VTl = VTile<D>;
   const char* Kt = stage;
@@ -142,10 +142,10 @@ __device__ __forceinline__ void flash_sub(const char* stage, int kt,
   bf16x8 p[NQ][2];
 #pragma unroll
   for (int qt = 0; qt < NQ; ++qt) {
-    if (MASK) {
+    if (__ballot(lim < 32)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (!valid(reg_key(r, half), qt)) s[qt][r] = -INFINITY;
+        if (reg_key(r, half) >= lim) s[qt][r] = -INFINITY;
     }
     float mx = fmaxf(s[qt][0], s[qt][1]);
 #pragma unroll
@@ -208,15 +208,38 @@ __device__ __forceinline__ void tile_barrier() {
 // Stage one K tile and one d-major V tile into LDS with direct global->LDS
 // 16-byte loads.  DMA number `blk` of a tile fills 1 KB of consecutive LDS rows;
 // lane j fetches the chunk that the swizzle puts at position j, so the layout
-// falls out of the source addresses alone.
-//   k_row(row)  element offset of key row `row` (0..63) in the K source
-//   v_col(c)    element offset, at d = 0, of the 8 keys of chunk c (0..7) in the
-//               d-major V source, whose d-rows are `v_ld` elements apart
-// Rows past the key list must still point at readable memory; the caller masks them.
-template <int D, class KRow, class VCol>
+// falls out of the source addresses alone.  Each lane stages NI key rows and NI
+// value chunks per tile; which ones is fixed by its lane and wave:
+template <int D>
+__device__ __forceinline__ int staged_k_row(int i) {   // key row (0..63) of K DMA i
+  using KTl = KTile<D>;
+  return ((threadIdx.x >> 6) * KTl::NI + i) * KTl::RPI + (threadIdx.x & 63) / KTl::CPR;
+}
+template <int D>
+__device__ __forceinline__ int staged_v_d(int i) {     // d-row of V DMA i
+  using VTl = VTile<D>;
+  return ((threadIdx.x >> 6) * VTl::NI + i) * VTl::RPI + (threadIdx.x & 63) / VTl::CPR;
+}
+template <int D>
+__device__ __forceinline__ int staged_v_chunk(int i) { // 8-key chunk (0..7) of V DMA i
+  using VTl = VTile<D>;
+  return ((threadIdx.x & 63) % VTl::CPR) ^ VTl::sw(staged_v_d<D>(i));
+}
+
+// Source element offsets of this lane's staged rows: k[i] of key row
+// staged_k_row(i), v[i] of the first of the 8 keys of chunk staged_v_chunk(i)
+// at d = 0 (the source's d-rows are v_ld elements apart).  Keys past the list
+// must still point at readable memory; the caller masks them.
+template <int D>
+struct TileSrc {
+  int64_t k[KTile<D>::NI];
+  int64_t v[VTile<D>::NI];
+};
+
+template <int D>
 __device__ __forceinline__ void stage_tile(char* stage, const uint16_t* kbase,
-                                           const uint16_t* vbase, int64_t v_ld, KRow k_row,
-                                           VCol v_col) {
+                                           const uint16_t* vbase, int64_t v_ld,
+                                           const TileSrc<D>& src) {
   using KTl = KTile<D>;
   using VTl = VTile<D>;
   const int wave = threadIdx.x >> 6;
@@ -224,16 +247,15 @@ __device__ __forceinline__ void stage_tile(char* stage, const uint16_t* kbase,
 #pragma unroll
   for (int i = 0; i < KTl::NI; ++i) {
     const int blk = wave * KTl::NI + i;
-    const int row = blk * KTl::RPI + lane / KTl::CPR;
+    const int row = staged_k_row<D>(i);
     const int c = (lane % KTl::CPR) ^ KTl::sw(row);
-    dma16(kbase + k_row(row) + 8 * c, stage + blk * 1024);
+    dma16(kbase + src.k[i] + 8 * c, stage + blk * 1024);
   }
 #pragma unroll
   for (int i = 0; i < VTl::NI; ++i) {
     const int blk = wave * VTl::NI + i;
-    const int d = blk * VTl::RPI + lane / VTl::CPR;
-    const int c = (lane % VTl::CPR) ^ VTl::sw(d);
-    dma16(vbase + v_col(c) + (int64_t)d * v_ld, stage + KTl::BYTES + blk * 1024);
+    dma16(vbase + src.v[i] + (int64_t)staged_v_d<D>(i) * v_ld,
+          stage + KTl::BYTES + blk * 1024);
   }
 }
 
@@ -374,59 +396,64 @@ phase1_kernel(P1Args a) {
   FlashState<D, NQ> st;
   flash_init(st);
 
-  // element offsets of key row `row` / key chunk `c` of tile t; keys past the
-  // list read the list's first key (masked out below)
-  auto k_off = [&](int t, int row) __attribute__((always_inline)) -> int64_t {
-    if (t < n_pre) {
-      const int e = t * KT + row;
-      return ((int64_t)krow[e < P ? e : 0] + kb_) * D;
-    }
-    const int kk = (t - n_pre) * KT + row;
-    return (own_k + (kk < own_end ? kk : 0)) * D;
-  };
-  auto v_off = [&](int t, int c) __attribute__((always_inline)) -> int64_t {
-    if (t < n_pre) {
-      const int e = t * KT + 8 * c;
-      return (int64_t)vcol[e < P ? e : 0] + vb_;
-    }
-    const int kk = (t - n_pre) * KT + 8 * c;
-    return own_v + (kk < own_end ? kk : 0);
-  };
-
-  stage_tile<D>(smem, kbase, vbase, v_ld,
-                [&](int row) __attribute__((always_inline)) { return k_off(0, row); },
-                [&](int c) __attribute__((always_inline)) { return v_off(0, c); });
-  const float sl2 = a.scale_log2;
-  for (int t = 0; t < n_tiles; ++t) {
-    tile_barrier();  // tile t has landed for every wave; tile t-1 is no longer read
-    if (t + 1 < n_tiles)
-      stage_tile<D>(smem + ((t + 1) & 1) * Stage<D>::BYTES, kbase, vbase, v_ld,
-                    [&](int row) __attribute__((always_inline)) { return k_off(t + 1, row); },
-                    [&](int c) __attribute__((always_inline)) { return v_off(t + 1, c); });
-    const char* stg = smem + (t & 1) * Stage<D>::BYTES;
+  // Staging addresses.  A prefix tile takes its key positions from the prefix
+  // lists; the list entries of tile t+1 are loaded one iteration ahead (raw
+  // registers), so the barrier's wait already covers them and no DMA waits on a
+  // list load.  Keys past the list read the list's first key (masked below).
+  constexpr int KNI = KTile<D>::NI, VNI = VTile<D>::NI;
+  int32_t rk[KNI], rv[VNI];
+  auto fetch_raw = [&](int t) __attribute__((always_inline)) {
     if (t < n_pre) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int e1 = t * KT + kt * 32;
-        if (e1 >= P) break;
-        if (e1 + 32 > P)
-          flash_sub<D, NQ, true>(stg, kt, qf, st, sl2, [&](int key, int) { return e1 + key < P; });
-        else
-          flash_sub<D, NQ, false>(stg, kt, qf, st, sl2, [](int, int) { return true; });
+      for (int x = 0; x < KNI; ++x) {
+        const int e = t * KT + staged_k_row<D>(x);
+        rk[x] = krow[e < P ? e : 0];
+      }
+#pragma unroll
+      for (int x = 0; x < VNI; ++x) {
+        const int e = t * KT + 8 * staged_v_chunk<D>(x);
+        rv[x] = vcol[e < P ? e : 0];
       }
     } else {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int k1 = (t - n_pre) * KT + kt * 32;
-        if (k1 > r0 + 31 || k1 >= own_end) break;  // above this wave's diagonal or past the block
-        if (k1 + 31 > r0 || k1 + 32 > own_end)
-          flash_sub<D, NQ, true>(stg, kt, qf, st, sl2, [&](int key, int) {
-            const int kk = k1 + key;
-            return kk <= r0 + lr && kk < own_end;
-          });
-        else
-          flash_sub<D, NQ, false>(stg, kt, qf, st, sl2, [](int, int) { return true; });
+      for (int x = 0; x < KNI; ++x) {
+        const int kk = (t - n_pre) * KT + staged_k_row<D>(x);
+        rk[x] = kk < own_end ? kk : 0;
       }
+#pragma unroll
+      for (int x = 0; x < VNI; ++x) {
+        const int kk = (t - n_pre) * KT + 8 * staged_v_chunk<D>(x);
+        rv[x] = kk < own_end ? kk : 0;
+      }
+    }
+  };
+  auto src_of = [&](int t) __attribute__((always_inline)) {
+    TileSrc<D> sr;
+    const bool pre = t < n_pre;
+#pragma unroll
+    for (int x = 0; x < KNI; ++x) sr.k[x] = ((pre ? kb_ : own_k) + rk[x]) * D;
+#pragma unroll
+    for (int x = 0; x < VNI; ++x) sr.v[x] = (pre ? vb_ : own_v) + rv[x];
+    return sr;
+  };
+
+  fetch_raw(0);
+  stage_tile<D>(smem, kbase, vbase, v_ld, src_of(0));
+  if (n_tiles > 1) fetch_raw(1);
+  const float sl2 = a.scale_log2;
+  for (int t = 0; t < n_tiles; ++t) {
+    tile_barrier();  // tile t has landed for every wave; tile t-1 is no longer read
+    if (t + 1 < n_tiles) stage_tile<D>(smem + ((t + 1) & 1) * Stage<D>::BYTES, kbase, vbase, v_ld, src_of(t + 1));
+    if (t + 2 < n_tiles) fetch_raw(t + 2);
+    const char* stg = smem + (t & 1) * Stage<D>::BYTES;
+    const bool pre = t < n_pre;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // prefix: every listed key is visible; own block: keys up to the row (causal)
+      const int k1 = (pre ? t : t - n_pre) * KT + kt * 32;
+      const int lim = pre ? P - k1 : min(r0 + lr - k1 + 1, own_end - k1);
+      if (!__ballot(lim > 0)) break;   // past the list, or above this wave's diagonal
+      flash_sub<D, NQ>(stg, kt, qf, st, sl2, lim);
     }
   }
 
@@ -624,39 +651,35 @@ phase2_kernel(P2Args a) {
   FlashState<D, NQ> st;
   flash_init(st);
 
-  auto k_off = [&](int t, int row) __attribute__((always_inline)) -> int64_t {
-    const int kk = k0 + t * KT + row;
-    return (int64_t)(kk < k1 ? kk : k0) * k_ld;
+  // keys past the part read its first key (masked below)
+  auto src_of = [&](int t) __attribute__((always_inline)) {
+    TileSrc<D> sr;
+#pragma unroll
+    for (int x = 0; x < KTile<D>::NI; ++x) {
+      const int kk = k0 + t * KT + staged_k_row<D>(x);
+      sr.k[x] = (int64_t)(kk < k1 ? kk : k0) * k_ld;
+    }
+#pragma unroll
+    for (int x = 0; x < VTile<D>::NI; ++x) {
+      const int kk = k0 + t * KT + 8 * staged_v_chunk<D>(x);
+      sr.v[x] = kk < k1 ? kk : k0;
+    }
+    return sr;
   };
-  auto v_off = [&](int t, int c) __attribute__((always_inline)) -> int64_t {
-    const int kk = k0 + t * KT + 8 * c;
-    return (int64_t)(kk < k1 ? kk : k0);
-  };
-  stage_tile<D>(smem, kbase, vbase, v_ld,
-                [&](int row) __attribute__((always_inline)) { return k_off(0, row); },
-                [&](int c) __attribute__((always_inline)) { return v_off(0, c); });
+  stage_tile<D>(smem, kbase, vbase, v_ld, src_of(0));
   const float sl2 = a.scale_log2;
   for (int t = 0; t < n_tiles; ++t) {
     tile_barrier();
-    if (t + 1 < n_tiles)
-      stage_tile<D>(smem + ((t + 1) & 1) * Stage<D>::BYTES, kbase, vbase, v_ld,
-                    [&](int row) __attribute__((always_inline)) { return k_off(t + 1, row); },
-                    [&](int c) __attribute__((always_inline)) { return v_off(t + 1, c); });
+    if (t + 1 < n_tiles) stage_tile<D>(smem + ((t + 1) & 1) * Stage<D>::BYTES, kbase, vbase, v_ld, src_of(t + 1));
     if (!wave_active) continue;
     const char* stg = smem + (t & 1) * Stage<D>::BYTES;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      // a shard part sees all its keys; the self part sees query tokens 0..tok (causal)
       const int kb = k0 + t * KT + kt * 32;
-      if (kb >= k1) break;
-      if (self_part) {
-        flash_sub<D, NQ, true>(stg, kt, qf, st, sl2, [&](int key, int) {
-          return kb + key <= tok && kb + key < k1;
-        });
-      } else if (kb + 32 > k1) {
-        flash_sub<D, NQ, true>(stg, kt, qf, st, sl2, [&](int key, int) { return kb + key < k1; });
-      } else {
-        flash_sub<D, NQ, false>(stg, kt, qf, st, sl2, [](int, int) { return true; });
-      }
+      const int lim = self_part ? min(tok - kb + 1, k1 - kb) : k1 - kb;
+      if (!__ballot(lim > 0)) break;
+      flash_sub<D, NQ>(stg, kt, qf, st, sl2, lim);
     }
   }
 
