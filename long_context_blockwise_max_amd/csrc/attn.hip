@@ -3,7 +3,7 @@
 //
 // Both phases run one MFMA tile routine.  A workgroup is 8 waves, two per SIMD,
 // so that one wave's softmax (VALU) overlaps the other wave's matrix work.
-// All 8 waves share each 64-key K / V tile staged in LDS; each wave owns 32
+// All 8 waves share each KT-key K / V tile staged in LDS; each wave owns 32
 // query rows and keeps, per row, a running reference maximum, a running sum
 // and an fp32 output accumulator (online softmax, Milakov & Gimelshein, as the
 // Star Attention review names it).
@@ -24,7 +24,7 @@
 // XOR-swizzled so that fragment reads are bank-conflict free.
 //
 // Softmax runs in base 2: t = (q.k) * log2(e) / sqrt(d), p = exp2(t - m).  P is
-// rounded to bf16 for the PV MFMA; the running sum uses the fp32 p.
+// rounded to bf16 for the PV MFMA and the running sum adds the same rounded p.
 #include <math.h>
 
 #include <algorithm>
@@ -35,10 +35,11 @@
 namespace pulsar {
 
 constexpr int KT = 64;            // keys per LDS tile (one barrier per tile)
+constexpr int NSUB = KT / 32;     // 32-key subtiles per tile
 constexpr int NW = 8;             // waves per workgroup
 constexpr int NTHR = 64 * NW;
 
-// K tile: 64 key rows x D (row = 2D bytes)
+// K tile: KT key rows x D (row = 2D bytes)
 template <int D>
 struct KTile {
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
@@ -55,15 +56,17 @@ struct KTile {
   }
 };
 
-// V tile, d-major: D rows (one per d) x 64 keys (row = 128 bytes = 8 chunks of 8 keys)
+// V tile, d-major: D rows (one per d) x KT keys (a row holds KT / 8 chunks of 8 keys)
 template <int D>
 struct VTile {
   static constexpr int CPR = KT / 8;
   static constexpr int ROWB = 2 * KT;
   static constexpr int BYTES = D * ROWB;
-  static constexpr int RPI = 1024 / ROWB;     // 8 d-rows per DMA
+  static constexpr int RPI = 1024 / ROWB;     // d-rows per DMA
   static constexpr int NI = D / RPI / NW;
-  __device__ static __forceinline__ int sw(int r) { return (r >> 1) & 7; }
+  __device__ static __forceinline__ int sw(int r) {
+    return CPR == 16 ? ((4 * (r & 3)) ^ ((r >> 2) & 3)) : ((r >> 1) & 7);
+  }
   // byte offset of key chunk c (keys 8c .. 8c+7) of d-row r
   __device__ static __forceinline__ int off(int r, int c) { return r * ROWB + ((c ^ sw(r)) << 4); }
 };
@@ -110,7 +113,7 @@ __device__ __forceinline__ void flash_init(FlashState<D, NQ>& st) {
 // hold without loss, and O / l at the end is the same ratio either way.
 constexpr float kRescaleSlack = 8.f;
 
-// One 32-key subtile `kt` (0 or 1) of the staged tile.  Keys 0 .. lim-1 of the
+// One 32-key subtile `kt` (0 .. NSUB-1) of the staged tile.  Keys 0 .. lim-1 of the
 // subtile are visible to this lane's query row (lim >= 32: all of them); the
 // mask is applied only when some lane of the wave needs it.
 template <int D, int NQ>
@@ -448,7 +451,7 @@ phase1_kernel(P1Args a) {
     const char* stg = smem + (t & 1) * Stage<D>::BYTES;
     const bool pre = t < n_pre;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < NSUB; ++kt) {
       // prefix: every listed key is visible; own block: keys up to the row (causal)
       const int k1 = (pre ? t : t - n_pre) * KT + kt * 32;
       const int lim = pre ? P - k1 : min(r0 + lr - k1 + 1, own_end - k1);
@@ -674,7 +677,7 @@ phase2_kernel(P2Args a) {
     if (!wave_active) continue;
     const char* stg = smem + (t & 1) * Stage<D>::BYTES;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < NSUB; ++kt) {
       // a shard part sees all its keys; the self part sees query tokens 0..tok (causal)
       const int kb = k0 + t * KT + kt * 32;
       const int lim = self_part ? min(tok - kb + 1, k1 - kb) : k1 - kb;
