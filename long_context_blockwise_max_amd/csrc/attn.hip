@@ -24,7 +24,7 @@
 // XOR-swizzled so that fragment reads are bank-conflict free.
 //
 // Softmax runs in base 2: t = (q.k) * log2(e) / sqrt(d), p = exp2(t - m).  P is
-// rounded to bf16 for the PV MFMA and the running sum adds the same rounded p.
+// rounded to bf16 for the PV MFMA; the running sum uses the fp32 p.
 #include <math.h>
 
 #include <algorithm>
@@ -108,10 +108,35 @@ __device__ __forceinline__ void flash_init(FlashState<D, NQ>& st) {
   }
 }
 
-// The reference maximum only moves when a row's running maximum exceeds it by
-// more than 2^8; until then p = exp2(t - m) <= 256, which fp32 sums and bf16 P
-// hold without loss, and O / l at the end is the same ratio either way.
+// The reference maximum m only moves when a score exceeds it by more than the
+// slack (log2 units); until then p = exp2(t - m) <= 2^8, which fp32 sums and
+// bf16 P hold without loss, and O / l at the end is the same ratio either way.
 constexpr float kRescaleSlack = 8.f;
+constexpr float kRescaleBound = 256.f;   // 2^kRescaleSlack
+
+// p = exp2(s * sl2 - m) for the 16 scores of one accumulator, rounded to bf16
+// into the two PV operands; sum = the fp32 sum of the p.  (v_dot2_f32_bf16 would
+// add two rounded p per instruction, but interleaved with the MFMAs of this
+// loop it produced wrong sums, so plain adds are used.)
+template <int NQ>
+__device__ __forceinline__ void softmax_p(const f32x16& s, float sl2, float m, bf16x8 (&p)[2],
+                                          float& sum) {
+  const float neg_m = -m;
+  float acc = 0.f;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[8 * hh + 2 * e], sl2, neg_m));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[8 * hh + 2 * e + 1], sl2, neg_m));
+      w[e] = pack_bf16x2(e0, e1);
+      acc += e0 + e1;
+    }
+    p[hh] = __builtin_bit_cast(bf16x8, w);
+  }
+  sum = acc;
+}
 
 // One 32-key subtile `kt` (0 .. NSUB-1) of the staged tile.  Keys 0 .. lim-1 of the
 // subtile are visible to this lane's query row (lim >= 32: all of them); the
@@ -150,13 +175,20 @@ __device__ __forceinline__ void flash_sub(const char* stage, int kt,
       for (int r = 0; r < 16; ++r)
         if (reg_key(r, half) >= lim) s[qt][r] = -INFINITY;
     }
-    float mx = fmaxf(s[qt][0], s[qt][1]);
+    // Fast path: p against the current reference maximum m, no max reduction.
+    // Every p stays <= 2^kRescaleSlack unless a score rose more than the slack
+    // above m, and then this lane's subtile sum exceeds 2^kRescaleSlack too (or
+    // is inf / nan), which sends the wave to the slow path: exact maximum,
+    // rescale of O and l, p recomputed.  The first subtile always takes it (m
+    // starts at -1e30).
+    float sum;
+    softmax_p<NQ>(s[qt], sl2, st.m[qt], p[qt], sum);
+    if (__ballot(!(sum <= kRescaleBound))) {
+      float mx = fmaxf(s[qt][0], s[qt][1]);
 #pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[qt][r]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float tmax = mx * sl2;
-    if (__ballot(tmax > st.m[qt] + kRescaleSlack)) {
-      const float m_new = fmaxf(st.m[qt], tmax);
+      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[qt][r]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_new = fmaxf(st.m[qt], mx * sl2);
       const float alpha = __builtin_amdgcn_exp2f(st.m[qt] - m_new);
       st.m[qt] = m_new;
       st.l[qt] *= alpha;
@@ -164,24 +196,9 @@ __device__ __forceinline__ void flash_sub(const char* stage, int kt,
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.o[dt][qt][r] *= alpha;
-    }
-    const float neg_m = -st.m[qt];
-    float sum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(s[qt][r], sl2, neg_m));
-      s[qt][r] = e;
-      sum += e;
+      softmax_p<NQ>(s[qt], sl2, st.m[qt], p[qt], sum);
     }
     st.l[qt] += sum;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = pack_bf16x2(s[qt][8 * hh + 2 * e], s[qt][8 * hh + 2 * e + 1]);
-      p[qt][hh] = __builtin_bit_cast(bf16x8, w);
-    }
   }
 
 #pragma unroll
