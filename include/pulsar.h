@@ -124,6 +124,26 @@ int pulsar_phase1_encode(const pulsar_geom* g, const pulsar_attn* a, const uint1
                          float* o, uint16_t* k_cache, uint16_t* v_cache, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* The two halves of pulsar_phase1_encode, for callers that schedule or time
+ * them apart (same arguments, same workspace; encode is prepare then attend on
+ * one stream).
+ * pulsar_phase1_prepare writes the rotated keys into k_cache, the d-major
+ * values into v_cache, and the rotated queries, the prefix index lists
+ * (sink and kept chunks of earlier blocks, Section 2.1) and the work order into
+ * the workspace.
+ * pulsar_phase1_attend runs the attention of every block row over
+ * [sink || summaries || own block] from what prepare left in k_cache, v_cache
+ * and ws; it must follow a prepare of the same geometry on the same workspace
+ * and caches (stream-ordered), which it cannot check.
+ * Errors: as pulsar_phase1_encode. */
+int pulsar_phase1_prepare(const pulsar_geom* g, const pulsar_attn* a, const uint16_t* q,
+                          const uint16_t* k, const uint16_t* v, const int32_t* sel,
+                          uint16_t* k_cache, uint16_t* v_cache, void* ws, size_t ws_bytes,
+                          void* stream);
+int pulsar_phase1_attend(const pulsar_geom* g, const pulsar_attn* a, const uint16_t* k_cache,
+                         const uint16_t* v_cache, float* o, void* ws, size_t ws_bytes,
+                         void* stream);
+
 /* Number of partial results pulsar_phase2_query writes per sequence for this
  * shape: every shard is split into the same number of contiguous key ranges,
  * plus one part for the self shard when has_self != 0.  Returns <= 0 on error. */

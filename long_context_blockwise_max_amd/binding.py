@@ -22,6 +22,7 @@ PULSAR_EUNSUPPORTED = -4
 
 EXPORTED = (
     "pulsar_workspace_bytes", "pulsar_kept_chunks", "pulsar_select", "pulsar_phase1_encode",
+    "pulsar_phase1_prepare", "pulsar_phase1_attend",
     "pulsar_phase2_num_parts", "pulsar_phase2_workspace_bytes", "pulsar_phase2_query",
     "pulsar_lse_merge", "pulsar_strerror",
 )
@@ -65,6 +66,10 @@ def lib():
         L.pulsar_select.restype = ctypes.c_int
         L.pulsar_phase1_encode.argtypes = [G, A, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pulsar_phase1_encode.restype = ctypes.c_int
+        L.pulsar_phase1_prepare.argtypes = [G, A, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pulsar_phase1_prepare.restype = ctypes.c_int
+        L.pulsar_phase1_attend.argtypes = [G, A, vp, vp, vp, vp, sz, vp]
+        L.pulsar_phase1_attend.restype = ctypes.c_int
         L.pulsar_phase2_num_parts.argtypes = [A, i32, i32, i32, i32, i32]
         L.pulsar_phase2_num_parts.restype = i32
         L.pulsar_phase2_workspace_bytes.argtypes = [A, i32, i32, i32]
@@ -171,6 +176,32 @@ def pulsar_phase1_encode(geom: Geom, attn: Attn, q, k, v, sel, o, k_cache, v_cac
         _bf16(v_cache, L * hkv * d, "v_cache"), _ptr(ws, torch.uint8, 0, "ws"), ws.numel(),
         _stream(stream))
     _check(rc, "pulsar_phase1_encode")
+
+
+def pulsar_phase1_prepare(geom: Geom, attn: Attn, q, k, v, sel, k_cache, v_cache, ws,
+                          stream=None):
+    import torch
+    L = geom.n_blocks * geom.block_size
+    hq, hkv, d = attn.n_q_heads, attn.n_kv_heads, attn.head_dim
+    kept = pulsar_kept_chunks(geom)
+    rc = lib().pulsar_phase1_prepare(
+        ctypes.byref(geom), ctypes.byref(attn), _bf16(q, L * hq * d, "q"), _bf16(k, L * hkv * d, "k"),
+        _bf16(v, L * hkv * d, "v"),
+        _ptr(sel, torch.int32, geom.n_blocks * max(kept, 0), "sel", allow_none=True),
+        _bf16(k_cache, L * hkv * d, "k_cache"), _bf16(v_cache, L * hkv * d, "v_cache"),
+        _ptr(ws, torch.uint8, 0, "ws"), ws.numel(), _stream(stream))
+    _check(rc, "pulsar_phase1_prepare")
+
+
+def pulsar_phase1_attend(geom: Geom, attn: Attn, k_cache, v_cache, o, ws, stream=None):
+    import torch
+    L = geom.n_blocks * geom.block_size
+    hq, hkv, d = attn.n_q_heads, attn.n_kv_heads, attn.head_dim
+    rc = lib().pulsar_phase1_attend(
+        ctypes.byref(geom), ctypes.byref(attn), _bf16(k_cache, L * hkv * d, "k_cache"),
+        _bf16(v_cache, L * hkv * d, "v_cache"), _ptr(o, torch.float32, L * hq * d, "o"),
+        _ptr(ws, torch.uint8, 0, "ws"), ws.numel(), _stream(stream))
+    _check(rc, "pulsar_phase1_attend")
 
 
 def pulsar_phase2_num_parts(attn: Attn, batch, n_shards, shard_len, q_len, has_self) -> int:

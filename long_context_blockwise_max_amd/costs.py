@@ -64,3 +64,25 @@ def phase2_bytes(batch, n_shards, shard_len, q_len, n_q_heads, n_kv_heads, head_
 
 def phase2_kv_bytes(batch, n_shards, shard_len, n_kv_heads, head_dim) -> int:
     return batch * 2 * 2 * n_shards * n_kv_heads * shard_len * head_dim
+
+
+def phase1_kernel_bytes(n_blocks, block_size, sink, chunk, k, n_q_heads, n_kv_heads,
+                        head_dim) -> int:
+    """Least bytes the Phase-1 attention launch moves: rotated queries (bf16), the
+    block's keys and values (bf16) and each block's prefix keys and values once,
+    the prefix index lists (two int32 per entry) and the float32 output."""
+    L = n_blocks * block_size
+    q = 2 * L * n_q_heads * head_dim
+    kv = 2 * 2 * L * n_kv_heads * head_dim
+    p = sum(prefix_len(i, sink, chunk, k) for i in range(1, n_blocks))
+    pre = 2 * 2 * p * n_kv_heads * head_dim + 2 * 4 * p
+    o = 4 * L * n_q_heads * head_dim
+    return q + kv + pre + o
+
+
+def phase2_kernel_bytes(batch, n_shards, shard_len, q_len, n_q_heads, n_kv_heads, head_dim,
+                        with_self=True) -> int:
+    """Least bytes of the Phase-2 query launch: the method's Phase-2 bytes (retained
+    K/V, query, self K/V, merged output); split-KV partials are overhead on top."""
+    return phase2_bytes(batch, n_shards, shard_len, q_len, n_q_heads, n_kv_heads, head_dim,
+                        with_self)

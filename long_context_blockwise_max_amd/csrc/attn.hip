@@ -550,23 +550,30 @@ int64_t phase1_prefix_total(const Phase1Geometry& g) {
   return p1_list_start(g.n_blocks, g.sink_size, g.chunk_size * g.kept);
 }
 
-int launch_phase1(const Phase1Geometry& g, const uint16_t* q_rot, const uint16_t* k_cache,
-                  const uint16_t* v_cache, const int32_t* sel, int32_t* prefix_rows,
-                  int32_t* order, float* o, hipStream_t stream) {
+int launch_phase1_lists(const Phase1Geometry& g, const int32_t* sel, int32_t* prefix_rows,
+                        int32_t* order, hipStream_t stream) {
   const int n_pairs = g.n_blocks * g.n_row_tiles;
   hipLaunchKernelGGL(phase1_order, dim3((n_pairs + 255) / 256), dim3(256), 0, stream, g.n_blocks,
                      g.block_size, g.chunk_size, g.kept, g.sink_size, g.rows_per_wg,
                      g.n_row_tiles, order);
   const int64_t total = phase1_prefix_total(g);
-  int32_t* krow = prefix_rows;
-  int32_t* vcol = prefix_rows + total;
   if (g.n_blocks > 1 && total > 0) {
     const int p_max = g.sink_size + g.chunk_size * g.kept * (g.n_blocks - 1);
     const int gx = (int)std::min<int64_t>(1024, ((int64_t)p_max + 255) / 256);
     hipLaunchKernelGGL(phase1_prefix_list, dim3(gx, g.n_blocks - 1), dim3(256), 0, stream, sel,
                        g.block_size, g.chunk_size, g.kept, g.sink_size, g.n_kv_heads, g.head_dim,
-                       krow, vcol);
+                       prefix_rows, prefix_rows + total);
   }
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int launch_phase1_attend(const Phase1Geometry& g, const uint16_t* q_rot, const uint16_t* k_cache,
+                         const uint16_t* v_cache, const int32_t* prefix_rows,
+                         const int32_t* order, float* o, hipStream_t stream) {
+  const int n_pairs = g.n_blocks * g.n_row_tiles;
+  const int64_t total = phase1_prefix_total(g);
+  const int32_t* krow = prefix_rows;
+  const int32_t* vcol = prefix_rows + total;
   P1Args a;
   a.q = q_rot;
   a.kc = k_cache;

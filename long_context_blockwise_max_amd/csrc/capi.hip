@@ -149,37 +149,102 @@ int pulsar_select(const pulsar_geom* g, const int32_t* tok, int32_t* sel, int32_
              : PULSAR_EHIP;
 }
 
-int pulsar_phase1_encode(const pulsar_geom* g, const pulsar_attn* a, const uint16_t* q,
-                         const uint16_t* k, const uint16_t* v, const int32_t* sel, float* o,
-                         uint16_t* k_cache, uint16_t* v_cache, void* ws, size_t ws_bytes,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// shared checks of the three Phase-1 calls; fills the workspace pointers
+struct P1Ws {
+  uint16_t* q_rot;
+  int32_t* lists;
+  int32_t* order;
+  Phase1Geometry pg;
+};
+
+int phase1_common(const pulsar_geom* g, const pulsar_attn* a, const uint16_t* k_cache,
+                  const uint16_t* v_cache, void* ws, size_t ws_bytes, P1Ws* out) {
   int rc = check_geom(g);
   if (rc) return rc;
   rc = check_attn(a);
   if (rc) return rc;
   rc = check_pair(g, a);
   if (rc) return rc;
-  const int32_t kept = kept_chunks(g);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(k_cache) ||
-      !aligned16(v_cache))
-    return PULSAR_EINVAL;
-  if (g->n_blocks > 1 && kept > 0 && !aligned16(sel)) return PULSAR_EINVAL;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PULSAR_EINVAL;
   const Layout l = layout(g, a);
   if (!ws || ws_bytes < l.total) return PULSAR_EWORKSPACE;
   if (!aligned16(ws)) return PULSAR_EINVAL;
   char* w = static_cast<char*>(ws);
-  uint16_t* q_rot = reinterpret_cast<uint16_t*>(w + l.q_rot);
-  int32_t* lists = reinterpret_cast<int32_t*>(w + l.lists);
-  int32_t* order = reinterpret_cast<int32_t*>(w + l.order);
-  const int64_t L = (int64_t)g->n_blocks * g->block_size;
-  hipStream_t s = as_stream(stream);
-  if (launch_rope_fill(q, k, v, L, g->block_size, a->n_q_heads, a->n_kv_heads, a->head_dim,
-                       a->rope_base, q_rot, k_cache, v_cache, s))
-    return PULSAR_EHIP;
-  Phase1Geometry pg = phase1_geometry(g->n_blocks, g->block_size, g->chunk_size, kept,
-                                      g->sink_size, a->n_q_heads, a->n_kv_heads, a->head_dim);
-  if (launch_phase1(pg, q_rot, k_cache, v_cache, sel, lists, order, o, s)) return PULSAR_EHIP;
+  out->q_rot = reinterpret_cast<uint16_t*>(w + l.q_rot);
+  out->lists = reinterpret_cast<int32_t*>(w + l.lists);
+  out->order = reinterpret_cast<int32_t*>(w + l.order);
+  out->pg = phase1_geometry(g->n_blocks, g->block_size, g->chunk_size, kept_chunks(g),
+                            g->sink_size, a->n_q_heads, a->n_kv_heads, a->head_dim);
   return PULSAR_OK;
+}
+
+int phase1_prepare_checked(const pulsar_geom* g, const pulsar_attn* a, const uint16_t* q,
+                           const uint16_t* k, const uint16_t* v, const int32_t* sel,
+                           uint16_t* k_cache, uint16_t* v_cache, const P1Ws& w, hipStream_t s) {
+  const int64_t L = (int64_t)g->n_blocks * g->block_size;
+  if (launch_rope_fill(q, k, v, L, g->block_size, a->n_q_heads, a->n_kv_heads, a->head_dim,
+                       a->rope_base, w.q_rot, k_cache, v_cache, s))
+    return PULSAR_EHIP;
+  if (launch_phase1_lists(w.pg, sel, w.lists, w.order, s)) return PULSAR_EHIP;
+  return PULSAR_OK;
+}
+
+int prepare_pointers_ok(const pulsar_geom* g, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const int32_t* sel) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return PULSAR_EINVAL;
+  if (g->n_blocks > 1 && kept_chunks(g) > 0 && !aligned16(sel)) return PULSAR_EINVAL;
+  return PULSAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pulsar_phase1_prepare(const pulsar_geom* g, const pulsar_attn* a, const uint16_t* q,
+                          const uint16_t* k, const uint16_t* v, const int32_t* sel,
+                          uint16_t* k_cache, uint16_t* v_cache, void* ws, size_t ws_bytes,
+                          void* stream) {
+  P1Ws w;
+  int rc = phase1_common(g, a, k_cache, v_cache, ws, ws_bytes, &w);
+  if (rc) return rc;
+  rc = prepare_pointers_ok(g, q, k, v, sel);
+  if (rc) return rc;
+  return phase1_prepare_checked(g, a, q, k, v, sel, k_cache, v_cache, w, as_stream(stream));
+}
+
+int pulsar_phase1_attend(const pulsar_geom* g, const pulsar_attn* a, const uint16_t* k_cache,
+                         const uint16_t* v_cache, float* o, void* ws, size_t ws_bytes,
+                         void* stream) {
+  P1Ws w;
+  int rc = phase1_common(g, a, k_cache, v_cache, ws, ws_bytes, &w);
+  if (rc) return rc;
+  if (!aligned16(o)) return PULSAR_EINVAL;
+  return launch_phase1_attend(w.pg, w.q_rot, k_cache, v_cache, w.lists, w.order, o,
+                              as_stream(stream))
+             ? PULSAR_EHIP
+             : PULSAR_OK;
+}
+
+int pulsar_phase1_encode(const pulsar_geom* g, const pulsar_attn* a, const uint16_t* q,
+                         const uint16_t* k, const uint16_t* v, const int32_t* sel, float* o,
+                         uint16_t* k_cache, uint16_t* v_cache, void* ws, size_t ws_bytes,
+                         void* stream) {
+  P1Ws w;
+  int rc = phase1_common(g, a, k_cache, v_cache, ws, ws_bytes, &w);
+  if (rc) return rc;
+  rc = prepare_pointers_ok(g, q, k, v, sel);
+  if (rc) return rc;
+  if (!aligned16(o)) return PULSAR_EINVAL;
+  const hipStream_t s = as_stream(stream);
+  rc = phase1_prepare_checked(g, a, q, k, v, sel, k_cache, v_cache, w, s);
+  if (rc) return rc;
+  return launch_phase1_attend(w.pg, w.q_rot, k_cache, v_cache, w.lists, w.order, o, s)
+             ? PULSAR_EHIP
+             : PULSAR_OK;
 }
 
 int32_t pulsar_phase2_num_parts(const pulsar_attn* a, int32_t batch, int32_t n_shards,

@@ -34,9 +34,15 @@ Phase1Geometry phase1_geometry(int32_t n_blocks, int32_t block_size, int32_t chu
 // total number of prefix entries over all blocks (the prefix index list length)
 int64_t phase1_prefix_total(const Phase1Geometry& g);
 
-int launch_phase1(const Phase1Geometry& g, const uint16_t* q_rot, const uint16_t* k_cache,
-                  const uint16_t* v_cache, const int32_t* sel, int32_t* prefix_rows,
-                  int32_t* order, float* o, hipStream_t stream);
+// work order of the (block, row tile) pairs and the prefix index lists
+// (prefix_rows holds 2 * phase1_prefix_total entries: key rows, then value columns)
+int launch_phase1_lists(const Phase1Geometry& g, const int32_t* sel, int32_t* prefix_rows,
+                        int32_t* order, hipStream_t stream);
+
+// the attention kernel proper; reads what launch_rope_fill and launch_phase1_lists wrote
+int launch_phase1_attend(const Phase1Geometry& g, const uint16_t* q_rot, const uint16_t* k_cache,
+                         const uint16_t* v_cache, const int32_t* prefix_rows,
+                         const int32_t* order, float* o, hipStream_t stream);
 
 struct Phase2Geometry {
   int32_t batch, n_shards, shard_len, q_len, n_q_heads, n_kv_heads, head_dim;

@@ -120,6 +120,15 @@ class HotPath:
                                self.sel if self.kept > 0 else None, self.o,
                                self.k_cache[0], self.v_cache[0], self.ws, stream)
 
+    def phase1_prepare(self, stream=None):
+        B.pulsar_phase1_prepare(self.cgeom, self.cattn, self.q, self.k, self.v,
+                                self.sel if self.kept > 0 else None, self.k_cache[0],
+                                self.v_cache[0], self.ws, stream)
+
+    def phase1_attend(self, stream=None):
+        B.pulsar_phase1_attend(self.cgeom, self.cattn, self.k_cache[0], self.v_cache[0], self.o,
+                               self.ws, stream)
+
     def phase2(self, stream=None):
         g = self.geo
         B.pulsar_phase2_query(self.cattn, g.batch, g.n_blocks, g.block_size, self.qq, g.q_len,

@@ -110,6 +110,32 @@ def test_phase1_rejects_bad_arguments():
 
 
 @needs_lib
+def test_phase1_halves_reject_bad_arguments():
+    lib = B.lib()
+    g = geom()
+    ws = B.pulsar_workspace_bytes(g, ATTN)
+
+    def prep(gg, aa, ptrs, wsb):
+        return lib.pulsar_phase1_prepare(ctypes.byref(gg), ctypes.byref(aa), *ptrs, FAKE, wsb, None)
+
+    def att(gg, aa, ptrs, wsb):
+        return lib.pulsar_phase1_attend(ctypes.byref(gg), ctypes.byref(aa), *ptrs, FAKE, wsb, None)
+
+    assert prep(g, ATTN, [FAKE] * 6, ws - 1) == B.PULSAR_EWORKSPACE
+    assert att(g, ATTN, [FAKE] * 3, ws - 1) == B.PULSAR_EWORKSPACE
+    assert prep(geom(block_size=100), ATTN, [FAKE] * 6, ws) == B.PULSAR_EINVAL
+    assert att(g, B.make_attn(32, 8, 80, 5e5), [FAKE] * 3, ws) == B.PULSAR_EUNSUPPORTED
+    for i in range(6):
+        p = [FAKE] * 6
+        p[i] = None
+        assert prep(g, ATTN, p, ws) == B.PULSAR_EINVAL, i
+    for i in range(3):
+        p = [FAKE] * 3
+        p[i] = FAKE_MIS
+        assert att(g, ATTN, p, ws) == B.PULSAR_EINVAL, i
+
+
+@needs_lib
 def test_phase2_part_count_and_rejections():
     n = B.pulsar_phase2_num_parts(ATTN, 1, 8, 16384, 64, True)
     assert n >= 9 and (n - 1) % 8 == 0

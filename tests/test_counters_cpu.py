@@ -1,0 +1,43 @@
+"""Host logic of the counter summary: per-dispatch sums over counter instances,
+copy-kernel calibration, and the source-hash gate bench.py applies."""
+import csv
+import json
+
+import bench
+from long_context_blockwise_max_amd import counters
+
+HEAD = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+        "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+        "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+        "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+
+def _csv(path, counter, rows):
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(HEAD)
+        for disp, name, vals in rows:
+            for v in vals:          # several instances (e.g. one per L2 channel group)
+                w.writerow([disp, disp, "Agent 1", 1, 1, 1, 64, 1, name, 256, 0, 0, 8, 0, 16,
+                            counter, v, 0, 1])
+
+
+def test_summary_scales_by_copy_and_gates_on_source(tmp_path):
+    copy = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>(...)"
+    p1 = "void pulsar::phase1_kernel<128>(pulsar::P1Args)"
+    # copy of 1 MiB reads 1024 KiB reported as 512 + 512; phase1 twice
+    _csv(tmp_path / "f.csv", "FETCH_SIZE", [(1, copy, [512.0, 512.0]), (2, p1, [1000.0, 1000.0]),
+                                             (3, p1, [1500.0, 1500.0])])
+    _csv(tmp_path / "w.csv", "WRITE_SIZE", [(1, copy, [256.0, 256.0]), (2, p1, [100.0]),
+                                             (3, p1, [300.0])])
+    out, md = tmp_path / "t.json", tmp_path / "t.md"
+    counters.main(["--fetch", str(tmp_path / "f.csv"), "--write", str(tmp_path / "w.csv"),
+                   "--copy-mib", "1", "--workload", "tiny", "--out", str(out), "--summary", str(md),
+                   "--command", "rocprofv3 ..."])
+    rec = json.loads(out.read_text())
+    e = rec["kernels"]["tiny"]["phase1_kernel"]
+    assert e["dispatches"] == 2
+    assert e["fetch_bytes"] == 2500 * 1024          # fetch scale 1.0
+    assert e["write_bytes"] == 200 * 1024 * 2       # write scale 2.0
+    assert rec["source_hash"] == bench.kernel_source_hash()
+    assert "phase1_kernel" in md.read_text()

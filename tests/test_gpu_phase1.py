@@ -106,3 +106,20 @@ def test_phase1_full_size_sampled(name):
     rows = sample_rows(w, per_block_random=1 if w.n_blocks > 8 else 3, seed=w.seed,
                        sparse=w.n_blocks > 8)
     _sampled_compare(case, rows)
+
+
+def test_prepare_then_attend_equals_encode():
+    """The two halves of the Phase-1 call, issued apart, give encode's results bit for bit."""
+    torch = torch_cuda()
+    w = W.with_(W.CONFIGS["tiny"], name="split", **SMALL["ragged_g2_d64"])
+    case = Case(w)
+    case.run()
+    o, kc, vc = case.path.o.clone(), case.path.k_cache.clone(), case.path.v_cache.clone()
+    case.path.o.zero_()
+    case.path.k_cache.zero_()
+    case.path.v_cache.zero_()
+    case.path.phase1_prepare()
+    case.path.phase1_attend()
+    torch.cuda.synchronize()
+    assert torch.equal(case.path.k_cache, kc) and torch.equal(case.path.v_cache, vc)
+    assert torch.equal(case.path.o, o)
