@@ -291,15 +291,11 @@ int pulsar_phase2_query(const pulsar_attn* a, int32_t batch, int32_t n_shards, i
   uint16_t* k_rot = has_self ? reinterpret_cast<uint16_t*>(w + l.k_rot) : nullptr;
   uint16_t* v_t = has_self ? reinterpret_cast<uint16_t*>(w + l.v_t) : nullptr;
   hipStream_t s = as_stream(stream);
-  const int64_t tok = (int64_t)batch * q_len;
-  if (launch_rope_rows(qq, q_rot, tok, a->n_q_heads, a->head_dim, q_pos0, q_len, a->rope_base, s))
+  if ((int64_t)batch * q_len > INT32_MAX / 2) return PULSAR_EUNSUPPORTED;
+  if (launch_phase2_prep(qq, has_self ? k_self : nullptr, v_self, batch, q_len, a->n_q_heads,
+                         a->n_kv_heads, a->head_dim, q_pos0, a->rope_base, pg.self_pad, q_rot,
+                         k_rot, v_t, s))
     return PULSAR_EHIP;
-  if (has_self) {
-    if (launch_rope_rows(k_self, k_rot, tok, a->n_kv_heads, a->head_dim, q_pos0, q_len,
-                         a->rope_base, s) ||
-        launch_v_self_fill(v_self, batch, q_len, pg.self_pad, a->n_kv_heads, a->head_dim, v_t, s))
-      return PULSAR_EHIP;
-  }
   return launch_phase2(pg, q_rot, k_cache, v_cache, k_rot, v_t, o_part, lse_part, s) == 0
              ? PULSAR_OK
              : PULSAR_EHIP;

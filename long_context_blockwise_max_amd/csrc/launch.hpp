@@ -15,12 +15,13 @@ int launch_rope_fill(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
                      double rope_base, uint16_t* q_rot, uint16_t* k_cache, uint16_t* v_cache,
                      hipStream_t stream);
 
-int launch_v_self_fill(const uint16_t* v, int32_t batch, int32_t q_len, int32_t lq_pad,
-                       int32_t n_kv_heads, int32_t head_dim, uint16_t* vt, hipStream_t stream);
-
-int launch_rope_rows(const uint16_t* x, uint16_t* y, int64_t n_tok, int32_t heads,
-                     int32_t head_dim, int64_t pos0, int32_t tok_per_seq, double rope_base,
-                     hipStream_t stream);
+// Phase-2 prep: q_rot [B][Lq][Hq][d] and k_rot [B][Lq][Hkv][d] rotated at positions
+// pos0 + t; v_t the d-major self values [B][Hkv][d][lq_pad].  k_self == NULL: no self shard
+// (k_rot, v_self and v_t unused)
+int launch_phase2_prep(const uint16_t* qq, const uint16_t* k_self, const uint16_t* v_self,
+                       int32_t batch, int32_t q_len, int32_t n_q_heads, int32_t n_kv_heads,
+                       int32_t head_dim, int64_t pos0, double rope_base, int32_t lq_pad,
+                       uint16_t* q_rot, uint16_t* k_rot, uint16_t* v_t, hipStream_t stream);
 
 struct Phase1Geometry {
   int32_t n_blocks, block_size, chunk_size, kept, sink_size;

@@ -12,11 +12,12 @@
 //                re-laid out from [L][Hkv][d] to the per-block, per-head
 //                [N][Hkv][b][d] (the keys each block keeps)
 //   v_cache_fill the values each block keeps, d-major: [N][Hkv][d][b]
-//   rope_rows    Phase-2 prep: rotate query-host rows [T][H][d] at positions
-//                pos0 + (t % tok_per_seq)
+//   phase2_prep  Phase-2 prep in one launch: rotated query rows and rotated
+//                self keys (positions pos0 + t), and the d-major copy of the
+//                self values
 //
-// One thread per (token, 8-wide pair chunk c): it derives cos/sin for the 8
-// frequencies 8c .. 8c+7 once and applies them to elements [8c, 8c+8) and
+// In rope_fill one thread per (token, 8-wide pair chunk c) derives cos/sin for
+// the 8 frequencies 8c .. 8c+7 once and applies them to elements [8c, 8c+8) and
 // [d/2 + 8c, d/2 + 8c + 8) of every head of the token.
 #include "common.hpp"
 #include "launch.hpp"
@@ -78,26 +79,6 @@ __global__ void __launch_bounds__(256) rope_fill(const uint16_t* __restrict__ q,
   }
 }
 
-template <int D>
-__global__ void __launch_bounds__(256) rope_rows(const uint16_t* __restrict__ x,
-                                                 uint16_t* __restrict__ y, int64_t n_tok,
-                                                 int32_t heads, int64_t pos0, int32_t tok_per_seq,
-                                                 double base) {
-  constexpr int CPH = D / 16;
-  const int64_t n = n_tok * CPH;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int c = (int)(idx % CPH);
-    const int64_t t = idx / CPH;
-    float cs[8], sn[8];
-    chunk_angles<D>(pos0 + t % tok_per_seq, c, base, cs, sn);
-    for (int h = 0; h < heads; ++h) {
-      const int64_t r = (t * heads + h) * D;
-      rotate_chunk<D>(x + r, y + r, c, cs, sn);
-    }
-  }
-}
-
 // d-major V: v [T][Hkv][D] -> vt, element (t, h, d) at vt_index(t, h) + d * ld.
 // One workgroup transposes 64 tokens x D of one head through LDS; every thread
 // then writes 16-byte runs of 8 consecutive tokens of one d-row.  The 8 tokens
@@ -105,10 +86,8 @@ __global__ void __launch_bounds__(256) rope_rows(const uint16_t* __restrict__ x,
 // and the block length is a multiple of 8).
 template <int D, class Dst>
 __device__ __forceinline__ void transpose_tile(const uint16_t* __restrict__ v, int64_t n_tok,
-                                               int32_t n_kv, Dst dst) {
+                                               int32_t n_kv, int h, int64_t t0, Dst dst) {
   __shared__ uint16_t tile[64][D + 8];
-  const int h = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * 64;
   constexpr int CPR = D / 8;
   for (int idx = threadIdx.x; idx < 64 * CPR; idx += blockDim.x) {
     const int r = idx / CPR, c = idx % CPR;
@@ -134,29 +113,71 @@ template <int D>
 __global__ void __launch_bounds__(256) v_cache_fill(const uint16_t* __restrict__ v, int64_t L,
                                                     int32_t block_size, int32_t n_kv,
                                                     uint16_t* __restrict__ vc) {
-  transpose_tile<D>(v, L, n_kv, [&](int64_t t, int h, int d) {
+  transpose_tile<D>(v, L, n_kv, blockIdx.y, (int64_t)blockIdx.x * 64, [&](int64_t t, int h, int d) {
     const int64_t blk = t / block_size, w = t - blk * block_size;
     return vc + ((blk * n_kv + h) * D + d) * block_size + w;
   });
 }
 
-// query-host values [B][Lq][Hkv][D] -> [B][Hkv][D][lq_pad], zero past Lq
+// Phase-2 prep.  Workgroups [0, n_tok) take one query-host token each: the
+// first D/2 threads derive cos/sin of the token's position into LDS, then the
+// workgroup rotates its Hq query heads and (with a self shard) its Hkv key
+// heads, one 8-wide pair chunk per thread.  The remaining workgroups transpose
+// 64 self-value tokens of one (sequence, head) into the d-major copy
+// [B][Hkv][D][lq_pad], zero past Lq.
 template <int D>
-__global__ void __launch_bounds__(256) v_self_fill(const uint16_t* __restrict__ v, int32_t lq,
-                                                   int32_t lq_pad, int32_t n_kv,
+__global__ void __launch_bounds__(256) phase2_prep(const uint16_t* __restrict__ qq,
+                                                   const uint16_t* __restrict__ ks,
+                                                   const uint16_t* __restrict__ vs, int32_t lq,
+                                                   int32_t n_tok, int32_t hq, int32_t hkv,
+                                                   int64_t pos0, double base, int32_t lq_pad,
+                                                   uint16_t* __restrict__ q_rot,
+                                                   uint16_t* __restrict__ k_rot,
                                                    uint16_t* __restrict__ vt) {
-  const int bb = blockIdx.z;
-  const uint16_t* src = v + (int64_t)bb * lq * n_kv * D;
-  uint16_t* base = vt + (int64_t)bb * n_kv * D * lq_pad;
-  transpose_tile<D>(src, lq, n_kv, [&](int64_t t, int h, int d) {
-    return base + ((int64_t)h * D + d) * lq_pad + t;
+  constexpr int HALF = D / 2;
+  constexpr int CPH = HALF / 8;
+  if ((int)blockIdx.x < n_tok) {
+    __shared__ float cs_l[HALF], sn_l[HALF];
+    const int t = blockIdx.x;
+    const int64_t pos = pos0 + t % lq;
+    if ((int)threadIdx.x < HALF) rope_cos_sin(pos, threadIdx.x, HALF, base, &cs_l[threadIdx.x],
+                                              &sn_l[threadIdx.x]);
+    __syncthreads();
+    const int n_heads = hq + (ks ? hkv : 0);
+    for (int idx = threadIdx.x; idx < n_heads * CPH; idx += blockDim.x) {
+      const int h = idx / CPH, c = idx % CPH;
+      float cs[8], sn[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        cs[e] = cs_l[8 * c + e];
+        sn[e] = sn_l[8 * c + e];
+      }
+      if (h < hq) {
+        const int64_t r = ((int64_t)t * hq + h) * D;
+        rotate_chunk<D>(qq + r, q_rot + r, c, cs, sn);
+      } else {
+        const int64_t r = ((int64_t)t * hkv + (h - hq)) * D;
+        rotate_chunk<D>(ks + r, k_rot + r, c, cs, sn);
+      }
+    }
+    return;
+  }
+  // self values: workgroup -> (sequence, head, 64-token group)
+  const int n_grp = (lq + 63) / 64;
+  int w = blockIdx.x - n_tok;
+  const int grp = w % n_grp;
+  w /= n_grp;
+  const int h = w % hkv;
+  const int bb = w / hkv;
+  const uint16_t* src = vs + (int64_t)bb * lq * hkv * D;
+  uint16_t* base_t = vt + (int64_t)bb * hkv * D * lq_pad;
+  transpose_tile<D>(src, lq, hkv, h, (int64_t)grp * 64, [&](int64_t tt, int hh, int d) {
+    return base_t + ((int64_t)hh * D + d) * lq_pad + tt;
   });
-  // zero the padding columns [lq, lq_pad) of this workgroup's head
-  const int h = blockIdx.y;
-  if (blockIdx.x == 0)
+  if (grp == 0)
     for (int idx = threadIdx.x; idx < D * (lq_pad - lq); idx += blockDim.x) {
-      const int d = idx / (lq_pad - lq), t = lq + idx % (lq_pad - lq);
-      base[((int64_t)h * D + d) * lq_pad + t] = 0;
+      const int d = idx / (lq_pad - lq), tt = lq + idx % (lq_pad - lq);
+      base_t[((int64_t)h * D + d) * lq_pad + tt] = 0;
     }
 }
 
@@ -187,26 +208,19 @@ int launch_rope_fill(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-int launch_v_self_fill(const uint16_t* v, int32_t batch, int32_t q_len, int32_t lq_pad,
-                       int32_t n_kv_heads, int32_t head_dim, uint16_t* vt, hipStream_t stream) {
-  const dim3 grid((unsigned)((q_len + 63) / 64), (unsigned)n_kv_heads, (unsigned)batch);
+int launch_phase2_prep(const uint16_t* qq, const uint16_t* k_self, const uint16_t* v_self,
+                       int32_t batch, int32_t q_len, int32_t n_q_heads, int32_t n_kv_heads,
+                       int32_t head_dim, int64_t pos0, double rope_base, int32_t lq_pad,
+                       uint16_t* q_rot, uint16_t* k_rot, uint16_t* v_t, hipStream_t stream) {
+  const int32_t n_tok = batch * q_len;
+  const int32_t n_vt = k_self ? ((q_len + 63) / 64) * n_kv_heads * batch : 0;
+  const dim3 grid((unsigned)(n_tok + n_vt));
   if (head_dim == 128)
-    hipLaunchKernelGGL(v_self_fill<128>, grid, dim3(256), 0, stream, v, q_len, lq_pad, n_kv_heads, vt);
+    hipLaunchKernelGGL(phase2_prep<128>, grid, dim3(256), 0, stream, qq, k_self, v_self, q_len,
+                       n_tok, n_q_heads, n_kv_heads, pos0, rope_base, lq_pad, q_rot, k_rot, v_t);
   else
-    hipLaunchKernelGGL(v_self_fill<64>, grid, dim3(256), 0, stream, v, q_len, lq_pad, n_kv_heads, vt);
-  return hipGetLastError() == hipSuccess ? 0 : -3;
-}
-
-int launch_rope_rows(const uint16_t* x, uint16_t* y, int64_t n_tok, int32_t heads,
-                     int32_t head_dim, int64_t pos0, int32_t tok_per_seq, double rope_base,
-                     hipStream_t stream) {
-  const int64_t n = n_tok * (head_dim / 16);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(rope_rows<128>, dim3(grid_for(n, 256)), dim3(256), 0, stream, x, y, n_tok,
-                       heads, pos0, tok_per_seq, rope_base);
-  else
-    hipLaunchKernelGGL(rope_rows<64>, dim3(grid_for(n, 256)), dim3(256), 0, stream, x, y, n_tok,
-                       heads, pos0, tok_per_seq, rope_base);
+    hipLaunchKernelGGL(phase2_prep<64>, grid, dim3(256), 0, stream, qq, k_self, v_self, q_len,
+                       n_tok, n_q_heads, n_kv_heads, pos0, rope_base, lq_pad, q_rot, k_rot, v_t);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -77,16 +77,25 @@ def test_phase2_full_size_decode_batch():
 
 
 def test_merge_kernel_alone():
+    """Merge against the oracle's merge.  Empty parts (lse = -inf) carry NaN output
+    rows on the device: the definition gives them weight 0, so the oracle sees any
+    finite row there (zeros) and the kernel must not let the NaN through.  Part
+    counts above 64 exercise the lane-strided LSE pass."""
     torch = torch_cuda()
     from long_context_blockwise_max_amd import binding as B
     rng = np.random.default_rng(3)
-    for (bsz, n_parts, lq, hq, d) in [(2, 7, 5, 4, 64), (1, 33, 64, 32, 128), (3, 1, 1, 8, 128)]:
+    for (bsz, n_parts, lq, hq, d) in [(2, 7, 5, 4, 64), (1, 33, 64, 32, 128), (3, 1, 1, 8, 128),
+                                      (2, 70, 3, 8, 128), (1, 131, 2, 4, 64)]:
         o_part = rng.standard_normal((bsz, n_parts, lq, hq, d)).astype(np.float32)
         lse_part = (rng.standard_normal((bsz, n_parts, lq, hq)) * 30).astype(np.float32)
+        o_dev = o_part.copy()
         if n_parts > 1:
-            lse_part[:, 0, 0, 0] = -np.inf       # an empty part contributes nothing
+            for p in {0, n_parts // 2, n_parts - 1}:
+                lse_part[:, p, 0, 0] = -np.inf       # an empty part contributes nothing
+                o_part[:, p, 0, 0] = 0.0
+                o_dev[:, p, 0, 0] = np.nan
         dev = torch.device("cuda")
-        op, lp = torch.from_numpy(o_part).to(dev), torch.from_numpy(lse_part).to(dev)
+        op, lp = torch.from_numpy(o_dev).to(dev), torch.from_numpy(lse_part).to(dev)
         o = torch.empty((bsz, lq, hq, d), device=dev)
         lse = torch.empty((bsz, lq, hq), device=dev)
         log(f"[merge] B={bsz} parts={n_parts} Lq={lq} Hq={hq} d={d}")
@@ -95,3 +104,17 @@ def test_merge_kernel_alone():
         want_o, want_lse = OA.lse_merge(np.moveaxis(o_part, 1, 0), np.moveaxis(lse_part, 1, 0))
         assert_close(o.cpu().numpy(), want_o, "merge O", max_abs=1e-5, mean_abs=1e-6)
         assert_close(lse.cpu().numpy(), want_lse, "merge LSE", max_abs=1e-4, mean_abs=1e-5)
+
+
+def test_merge_of_only_empty_parts_is_zero_with_lse_minus_inf():
+    torch = torch_cuda()
+    from long_context_blockwise_max_amd import binding as B
+    dev = torch.device("cuda")
+    op = torch.full((1, 3, 1, 2, 64), float("nan"), device=dev)
+    lp = torch.full((1, 3, 1, 2), float("-inf"), device=dev)
+    o = torch.empty((1, 1, 2, 64), device=dev)
+    lse = torch.empty((1, 1, 2), device=dev)
+    B.pulsar_lse_merge(1, 3, 1, 2, 64, op, lp, o, lse)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0).item()
+    assert torch.all(lse == float("-inf")).item()
