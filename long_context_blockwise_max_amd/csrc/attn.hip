@@ -225,6 +225,23 @@ __device__ __forceinline__ void tile_barrier() {
   __syncthreads();
 }
 
+// gfx9 s_waitcnt immediate: vmcnt = n, lgkmcnt = 0, expcnt not waited on.
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
+// Barrier after which every load this wave issued before its newest N vector
+// memory loads has landed, and this wave's LDS reads are done.  The wait is the
+// builtin, so the compiler's own wait bookkeeping knows about it; the s_barrier
+// carries no fence (the fence of __syncthreads() waits for every outstanding
+// load, tiles still in flight included); the empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void tile_barrier_n() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(N));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Stage one K tile and one d-major V tile into LDS with direct global->LDS
 // 16-byte loads.  DMA number `blk` of a tile fills 1 KB of consecutive LDS rows;
 // lane j fetches the chunk that the swizzle puts at position j, so the layout
@@ -616,11 +633,18 @@ struct P2Args {
   float scale_log2;
 };
 
-template <int D>
+// KSPLIT: the decode form (all query rows of the workgroup in one 32-row wave),
+// chosen by the launcher; two waves then split the subtiles of every tile.
+template <int D, bool KSPLIT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NTHR, NTHR), amdgpu_waves_per_eu(2, 2)))
 phase2_kernel(P2Args a) {
   constexpr int NQ = 1;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * Stage<D>::BYTES];
+  // Tile slots.  The decode form streams its part from HBM with little work per
+  // tile, so its loads run two tiles ahead (three slots); otherwise one tile
+  // ahead (two slots).
+  constexpr int NSLOT = KSPLIT ? 3 : 2;
+  constexpr int AHEAD = NSLOT - 1;
+  __shared__ __attribute__((aligned(1024))) char smem[NSLOT * Stage<D>::BYTES];
 
   int w = blockIdx.x;
   const int p = w % a.n_parts;
@@ -632,7 +656,12 @@ phase2_kernel(P2Args a) {
   const int wave = threadIdx.x >> 6;
   const int lr = threadIdx.x & 31;
   const int n_rows = a.group * a.lq;
-  const int row_base = rg * (NW * 32) + wave * 32;
+  // Decode shapes (every query row of the workgroup fits one 32-row wave): two
+  // waves share the rows and take one of the two subtiles of every tile each,
+  // so the matrix work per tile is split; their partial states are combined
+  // exactly at the end.
+  constexpr bool key_split = KSPLIT;
+  const int row_base = key_split ? 0 : rg * (NW * 32) + wave * 32;
 
   // key source of this part: a contiguous range of one retained shard, or the
   // query tokens' own keys, attended causally
@@ -663,7 +692,7 @@ phase2_kernel(P2Args a) {
 
   // query fragments: row fr = head-in-group * Lq + token
   bf16x8 qf[NQ][D / 16];
-  const bool wave_active = row_base < n_rows;
+  const bool wave_active = key_split ? wave < NSUB : row_base < n_rows;
   const int fr = row_base + lr;
   {
     const uint16_t* qrow = nullptr;
@@ -693,21 +722,60 @@ phase2_kernel(P2Args a) {
     }
     return sr;
   };
-  stage_tile<D>(smem, kbase, vbase, v_ld, src_of(0));
+  // Every iteration issues the same ND loads per wave (tiles past the part are
+  // staged into a free slot and never read), so at each barrier exactly the
+  // loads of the AHEAD - 1 newest tiles may still be in flight.
+  constexpr int ND = KTile<D>::NI + VTile<D>::NI;
+  auto slot = [&](int t) __attribute__((always_inline)) { return smem + (t % NSLOT) * Stage<D>::BYTES; };
+#pragma unroll
+  for (int u = 0; u < AHEAD; ++u) stage_tile<D>(slot(u), kbase, vbase, v_ld, src_of(u));
   const float sl2 = a.scale_log2;
   for (int t = 0; t < n_tiles; ++t) {
-    tile_barrier();
-    if (t + 1 < n_tiles) stage_tile<D>(smem + ((t + 1) & 1) * Stage<D>::BYTES, kbase, vbase, v_ld, src_of(t + 1));
+    tile_barrier_n<(AHEAD - 1) * ND>();   // tile t has landed; every wave is past its reads of tile t-1
+    stage_tile<D>(slot(t + AHEAD), kbase, vbase, v_ld, src_of(t + AHEAD));   // into the slot of tile t-1
     if (!wave_active) continue;
-    const char* stg = smem + (t & 1) * Stage<D>::BYTES;
+    const char* stg = slot(t);
 #pragma unroll
     for (int kt = 0; kt < NSUB; ++kt) {
+      if (key_split && kt != wave) continue;
       // a shard part sees all its keys; the self part sees query tokens 0..tok (causal)
       const int kb = k0 + t * KT + kt * 32;
       const int lim = self_part ? min(tok - kb + 1, k1 - kb) : k1 - kb;
       if (!__ballot(lim > 0)) break;
       flash_sub<D, NQ>(stg, kt, qf, st, sl2, lim);
     }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may land after the workgroup ends
+
+  if (key_split) {
+    // Wave 1 hands its state to wave 0 through LDS (every wave is past its last
+    // read of the slots); wave 0 merges: m = max(m0, m1), O and l rescaled by
+    // exp2(m_i - m) and added.  Both waves hold the same rows in the same lanes.
+    constexpr int NO = D / 32 * 16;   // accumulator floats per lane
+    float* xf = reinterpret_cast<float*>(smem);
+    const int lane = threadIdx.x & 63;
+    __syncthreads();
+    if (wave == 1) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xf[(dt * 16 + r) * 64 + lane] = st.o[dt][0][r];
+      xf[NO * 64 + lane] = st.m[0];
+      xf[(NO + 1) * 64 + lane] = st.l[0];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const float m1 = xf[NO * 64 + lane];
+    const float m = fmaxf(st.m[0], m1);
+    const float a0 = __builtin_amdgcn_exp2f(st.m[0] - m);
+    const float a1 = __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        st.o[dt][0][r] = st.o[dt][0][r] * a0 + xf[(dt * 16 + r) * 64 + lane] * a1;
+    st.l[0] = st.l[0] * a0 + xf[(NO + 1) * 64 + lane] * a1;
+    st.m[0] = m;
   }
 
   if (!wave_active) return;
@@ -775,10 +843,14 @@ int launch_phase2(const Phase2Geometry& g, const uint16_t* q_rot, const uint16_t
   a.n_rg = g.n_row_groups;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.head_dim));
   const int64_t grid = (int64_t)g.batch * g.n_kv_heads * g.n_row_groups * g.n_parts;
-  if (g.head_dim == 128)
-    hipLaunchKernelGGL(phase2_kernel<128>, dim3(grid), dim3(NTHR), 0, stream, a);
-  else
-    hipLaunchKernelGGL(phase2_kernel<64>, dim3(grid), dim3(NTHR), 0, stream, a);
+  const bool ksplit = g.n_row_groups == 1 && (g.n_q_heads / g.n_kv_heads) * g.q_len <= 32;
+  if (g.head_dim == 128) {
+    if (ksplit) hipLaunchKernelGGL((phase2_kernel<128, true>), dim3(grid), dim3(NTHR), 0, stream, a);
+    else hipLaunchKernelGGL((phase2_kernel<128, false>), dim3(grid), dim3(NTHR), 0, stream, a);
+  } else {
+    if (ksplit) hipLaunchKernelGGL((phase2_kernel<64, true>), dim3(grid), dim3(NTHR), 0, stream, a);
+    else hipLaunchKernelGGL((phase2_kernel<64, false>), dim3(grid), dim3(NTHR), 0, stream, a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -49,6 +49,12 @@ SMALL = {
                          q_len=64, budget_chunks=2, n_planted=0),
     "g8_d128_lq40": dict(n_blocks=2, block_size=384, n_q_heads=8, n_kv_heads=1, head_dim=128,
                          q_len=40, budget_chunks=2, n_planted=0),
+    # decode form (every query row of a KV head in one 32-row wave, two waves
+    # splitting each tile's subtiles): a 32-key part leaves the second wave empty
+    "decode_d128_short": dict(n_blocks=3, block_size=96, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                              q_len=1, batch=2, budget_chunks=1, n_planted=0),
+    "decode_rows32": dict(n_blocks=3, block_size=256, n_q_heads=8, n_kv_heads=2, q_len=8,
+                          budget_chunks=2, n_planted=0),
 }
 
 
