@@ -640,9 +640,9 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(NTHR, NTHR), amdgpu_w
 phase2_kernel(P2Args a) {
   constexpr int NQ = 1;
   // Tile slots.  The decode form streams its part from HBM with little work per
-  // tile, so its loads run two tiles ahead (three slots); otherwise one tile
-  // ahead (two slots).
-  constexpr int NSLOT = KSPLIT ? 3 : 2;
+  // tile, so its loads run three tiles ahead (four slots, 128 KB at d = 128);
+  // otherwise one tile ahead (two slots).
+  constexpr int NSLOT = KSPLIT ? 4 : 2;
   constexpr int AHEAD = NSLOT - 1;
   __shared__ __attribute__((aligned(1024))) char smem[NSLOT * Stage<D>::BYTES];
 
