@@ -179,6 +179,45 @@ int pulsar_phase2_query(const pulsar_attn* a, int32_t batch, int32_t n_shards,
                         float* lse_part, int32_t n_parts, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* Generation ("Dropping the Anchor ..." Section 2.2, with the generated tokens
+ * of Section 5's --tokens_to_generate): the query host keeps its own tokens --
+ * the query, then every generated token -- in a self cache, and each new token
+ * attends to every retained shard plus, causally, the self cache.
+ *
+ * pulsar_self_append appends n_new tokens to self caches that hold n_self:
+ *   k_new, v_new   [B][n_new][Hkv][d] bf16, pre-RoPE; token j sits at position
+ *                  self_pos0 + n_self + j (self_pos0 = position of self token 0)
+ *   k_self_cache   [B][cap][Hkv][d] bf16: receives the rotated keys
+ *   v_self_cache   [B][Hkv][d][cap] bf16, d-major: receives the values; the
+ *                  columns from n_self + n_new up to the next multiple of 8 are
+ *                  zeroed (the attention reads values in runs of 8 tokens), so
+ *                  these caches must only be written through this call
+ *   cap            capacity in tokens, a multiple of 8; n_self + n_new <= cap
+ * Errors: PULSAR_EINVAL, PULSAR_EUNSUPPORTED, PULSAR_EHIP. */
+int pulsar_self_append(const pulsar_attn* a, int32_t batch, int32_t cap, int32_t n_self,
+                       int32_t n_new, int64_t self_pos0, const uint16_t* k_new,
+                       const uint16_t* v_new, uint16_t* k_self_cache, uint16_t* v_self_cache,
+                       void* stream);
+
+/* Phase-2 attention of the last q_len self tokens (1 <= q_len <= n_self; one
+ * generated token per step is q_len = 1).  Query token t is self token
+ * n_self - q_len + t, at position self_pos0 + n_self - q_len + t; it attends to
+ * every key of the retained shards and to self tokens 0 .. n_self - q_len + t.
+ * Writes partials exactly as pulsar_phase2_query with a self shard (its last
+ * part is the self cache), to be merged with pulsar_lse_merge.
+ *   qq                 [B][q_len][Hq][d] bf16, pre-RoPE
+ *   k_cache, v_cache   retained shards, as in pulsar_phase2_query
+ *   k_self_cache, v_self_cache, cap   filled by pulsar_self_append, n_self tokens
+ *   n_parts            pulsar_phase2_num_parts(a, batch, n_shards, shard_len, q_len, 1)
+ *   ws                 at least pulsar_phase2_workspace_bytes(a, batch, q_len, 0) bytes
+ * Errors: PULSAR_EINVAL, PULSAR_EWORKSPACE, PULSAR_EUNSUPPORTED, PULSAR_EHIP. */
+int pulsar_phase2_decode(const pulsar_attn* a, int32_t batch, int32_t n_shards,
+                         int32_t shard_len, const uint16_t* qq, int32_t q_len,
+                         const uint16_t* k_cache, const uint16_t* v_cache,
+                         const uint16_t* k_self_cache, const uint16_t* v_self_cache, int32_t cap,
+                         int32_t n_self, int64_t self_pos0, float* o_part, float* lse_part,
+                         int32_t n_parts, void* ws, size_t ws_bytes, void* stream);
+
 /* Exact log-sum-exp merge of partial attention results (the Star Attention
  * review's corrected update: weight exp(s_h - s_global) on the normalised A_h):
  *   lse = ln sum_p exp(lse_part[p]),  o = sum_p exp(lse_part[p] - lse) * o_part[p]

@@ -22,7 +22,7 @@ PULSAR_EUNSUPPORTED = -4
 
 EXPORTED = (
     "pulsar_workspace_bytes", "pulsar_kept_chunks", "pulsar_select", "pulsar_phase1_encode",
-    "pulsar_phase1_prepare", "pulsar_phase1_attend",
+    "pulsar_phase1_prepare", "pulsar_phase1_attend", "pulsar_self_append", "pulsar_phase2_decode",
     "pulsar_phase2_num_parts", "pulsar_phase2_workspace_bytes", "pulsar_phase2_query",
     "pulsar_lse_merge", "pulsar_strerror",
 )
@@ -77,6 +77,11 @@ def lib():
         L.pulsar_phase2_query.argtypes = [A, i32, i32, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp,
                                           i32, vp, sz, vp]
         L.pulsar_phase2_query.restype = ctypes.c_int
+        L.pulsar_self_append.argtypes = [A, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp]
+        L.pulsar_self_append.restype = ctypes.c_int
+        L.pulsar_phase2_decode.argtypes = [A, i32, i32, i32, vp, i32, vp, vp, vp, vp, i32, i32, i64,
+                                           vp, vp, i32, vp, sz, vp]
+        L.pulsar_phase2_decode.restype = ctypes.c_int
         L.pulsar_lse_merge.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.pulsar_lse_merge.restype = ctypes.c_int
         L.pulsar_strerror.argtypes = [ctypes.c_int]
@@ -233,6 +238,38 @@ def pulsar_phase2_query(attn: Attn, batch, n_shards, shard_len, qq, q_len, q_pos
         _ptr(o_part, torch.float32, rows * d, "o_part"), _ptr(lse_part, torch.float32, rows, "lse_part"),
         n_parts, _ptr(ws, torch.uint8, 0, "ws"), ws.numel(), _stream(stream))
     _check(rc, "pulsar_phase2_query")
+
+
+def pulsar_self_append(attn: Attn, batch, cap, n_self, n_new, self_pos0, k_new, v_new,
+                       k_self_cache, v_self_cache, stream=None):
+    hkv, d = attn.n_kv_heads, attn.head_dim
+    new_n = batch * n_new * hkv * d
+    cache_n = batch * cap * hkv * d
+    rc = lib().pulsar_self_append(
+        ctypes.byref(attn), batch, cap, n_self, n_new, int(self_pos0),
+        _bf16(k_new, new_n, "k_new"), _bf16(v_new, new_n, "v_new"),
+        _bf16(k_self_cache, cache_n, "k_self_cache"), _bf16(v_self_cache, cache_n, "v_self_cache"),
+        _stream(stream))
+    _check(rc, "pulsar_self_append")
+
+
+def pulsar_phase2_decode(attn: Attn, batch, n_shards, shard_len, qq, q_len, k_cache, v_cache,
+                         k_self_cache, v_self_cache, cap, n_self, self_pos0, o_part, lse_part,
+                         n_parts, ws, stream=None):
+    import torch
+    hq, hkv, d = attn.n_q_heads, attn.n_kv_heads, attn.head_dim
+    kv_n = batch * n_shards * hkv * shard_len * d
+    cache_n = batch * cap * hkv * d
+    rows = batch * n_parts * q_len * hq
+    rc = lib().pulsar_phase2_decode(
+        ctypes.byref(attn), batch, n_shards, shard_len, _bf16(qq, batch * q_len * hq * d, "qq"),
+        q_len, _bf16(k_cache, kv_n, "k_cache", allow_none=n_shards == 0),
+        _bf16(v_cache, kv_n, "v_cache", allow_none=n_shards == 0),
+        _bf16(k_self_cache, cache_n, "k_self_cache"), _bf16(v_self_cache, cache_n, "v_self_cache"),
+        cap, n_self, int(self_pos0), _ptr(o_part, torch.float32, rows * d, "o_part"),
+        _ptr(lse_part, torch.float32, rows, "lse_part"), n_parts, _ptr(ws, torch.uint8, 0, "ws"),
+        ws.numel(), _stream(stream))
+    _check(rc, "pulsar_phase2_decode")
 
 
 def pulsar_lse_merge(batch, n_parts, q_len, n_q_heads, head_dim, o_part, lse_part, o, lse,

@@ -625,11 +625,14 @@ struct P2Args {
   const uint16_t* q;    // [B][Lq][Hq][D], rotated
   const uint16_t* kc;   // [B][S][Hkv][n][D]
   const uint16_t* vc;   // [B][S][Hkv][D][n]
-  const uint16_t* ks;   // [B][Lq][Hkv][D] rotated, or null
-  const uint16_t* vs;   // [B][Hkv][D][lq_pad] d-major copy of the self values
+  const uint16_t* ks;   // self keys, rotated: token j of sequence b at ks + b * ks_seq + j * Hkv * D
+  const uint16_t* vs;   // self values, d-major: (b, head, d) row at vs + b * vs_seq + (head * D + d) * vs_ld
   float* o_part;        // [B][n_parts][Lq][Hq][D]
   float* lse_part;      // [B][n_parts][Lq][Hq]
-  int32_t batch, n_shards, n, lq, lq_pad, hq, hkv, group, splits, n_parts, n_rg;
+  int64_t ks_seq, vs_seq;
+  int32_t batch, n_shards, n, lq, hq, hkv, group, splits, n_parts, n_rg;
+  int32_t n_self;       // self tokens; the Lq queries are the last Lq of them
+  int32_t vs_ld;        // >= n_self rounded up to 8
   float scale_log2;
 };
 
@@ -682,11 +685,11 @@ phase2_kernel(P2Args a) {
     k_ld = D;
     v_ld = a.n;
   } else {
-    k1 = a.lq;
-    kbase = a.ks + ((int64_t)bb * a.lq * a.hkv + g) * D;
-    vbase = a.vs + ((int64_t)bb * a.hkv + g) * D * a.lq_pad;
+    k1 = a.n_self;
+    kbase = a.ks + (int64_t)bb * a.ks_seq + (int64_t)g * D;
+    vbase = a.vs + (int64_t)bb * a.vs_seq + (int64_t)g * D * a.vs_ld;
     k_ld = (int64_t)a.hkv * D;
-    v_ld = a.lq_pad;
+    v_ld = a.vs_ld;
   }
   const int n_tiles = (k1 - k0 + KT - 1) / KT;
 
@@ -738,9 +741,10 @@ phase2_kernel(P2Args a) {
 #pragma unroll
     for (int kt = 0; kt < NSUB; ++kt) {
       if (key_split && kt != wave) continue;
-      // a shard part sees all its keys; the self part sees query tokens 0..tok (causal)
+      // a shard part sees all its keys; the self part sees self tokens up to the
+      // query token itself (query token tok is self token n_self - Lq + tok)
       const int kb = k0 + t * KT + kt * 32;
-      const int lim = self_part ? min(tok - kb + 1, k1 - kb) : k1 - kb;
+      const int lim = self_part ? min(a.n_self - a.lq + tok - kb + 1, k1 - kb) : k1 - kb;
       if (!__ballot(lim > 0)) break;
       flash_sub<D, NQ>(stg, kt, qf, st, sl2, lim);
     }
@@ -820,21 +824,24 @@ Phase2Geometry phase2_geometry(int32_t batch, int32_t n_shards, int32_t shard_le
 }
 
 int launch_phase2(const Phase2Geometry& g, const uint16_t* q_rot, const uint16_t* k_cache,
-                  const uint16_t* v_cache, const uint16_t* k_self_rot, const uint16_t* v_self_t,
-                  float* o_part, float* lse_part, hipStream_t stream) {
+                  const uint16_t* v_cache, const SelfShard& self, float* o_part,
+                  float* lse_part, hipStream_t stream) {
   P2Args a;
   a.q = q_rot;
   a.kc = k_cache;
   a.vc = v_cache;
-  a.ks = k_self_rot;
-  a.vs = v_self_t;
+  a.ks = self.k;
+  a.vs = self.v;
+  a.ks_seq = self.k_seq;
+  a.vs_seq = self.v_seq;
+  a.n_self = self.n;
+  a.vs_ld = self.v_ld;
   a.o_part = o_part;
   a.lse_part = lse_part;
   a.batch = g.batch;
   a.n_shards = g.n_shards;
   a.n = g.shard_len;
   a.lq = g.q_len;
-  a.lq_pad = g.self_pad;
   a.hq = g.n_q_heads;
   a.hkv = g.n_kv_heads;
   a.group = g.n_q_heads / g.n_kv_heads;

@@ -296,9 +296,76 @@ int pulsar_phase2_query(const pulsar_attn* a, int32_t batch, int32_t n_shards, i
                          a->n_kv_heads, a->head_dim, q_pos0, a->rope_base, pg.self_pad, q_rot,
                          k_rot, v_t, s))
     return PULSAR_EHIP;
-  return launch_phase2(pg, q_rot, k_cache, v_cache, k_rot, v_t, o_part, lse_part, s) == 0
+  SelfShard self{};
+  if (has_self) {
+    self.k = k_rot;
+    self.v = v_t;
+    self.k_seq = (int64_t)q_len * a->n_kv_heads * a->head_dim;
+    self.v_seq = (int64_t)a->n_kv_heads * a->head_dim * pg.self_pad;
+    self.n = q_len;
+    self.v_ld = pg.self_pad;
+  }
+  return launch_phase2(pg, q_rot, k_cache, v_cache, self, o_part, lse_part, s) == 0 ? PULSAR_OK
+                                                                                       : PULSAR_EHIP;
+}
+
+int pulsar_self_append(const pulsar_attn* a, int32_t batch, int32_t cap, int32_t n_self,
+                       int32_t n_new, int64_t self_pos0, const uint16_t* k_new,
+                       const uint16_t* v_new, uint16_t* k_self_cache, uint16_t* v_self_cache,
+                       void* stream) {
+  if (check_attn(a) != PULSAR_OK) return check_attn(a);
+  if (batch < 1 || n_new < 1 || n_self < 0 || cap < 8 || self_pos0 < 0) return PULSAR_EINVAL;
+  if (cap % 8 != 0) return PULSAR_EUNSUPPORTED;   // values are read in runs of 8 tokens
+  if ((int64_t)n_self + n_new > cap) return PULSAR_EINVAL;
+  if ((int64_t)batch * n_new > INT32_MAX / 2) return PULSAR_EUNSUPPORTED;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_self_cache) || !aligned16(v_self_cache))
+    return PULSAR_EINVAL;
+  return launch_self_append(k_new, v_new, batch, n_new, n_self, cap, a->n_kv_heads, a->head_dim,
+                            self_pos0, a->rope_base, k_self_cache, v_self_cache,
+                            as_stream(stream)) == 0
              ? PULSAR_OK
              : PULSAR_EHIP;
+}
+
+int pulsar_phase2_decode(const pulsar_attn* a, int32_t batch, int32_t n_shards,
+                         int32_t shard_len, const uint16_t* qq, int32_t q_len,
+                         const uint16_t* k_cache, const uint16_t* v_cache,
+                         const uint16_t* k_self_cache, const uint16_t* v_self_cache, int32_t cap,
+                         int32_t n_self, int64_t self_pos0, float* o_part, float* lse_part,
+                         int32_t n_parts, void* ws, size_t ws_bytes, void* stream) {
+  const int32_t want = pulsar_phase2_num_parts(a, batch, n_shards, shard_len, q_len, 1);
+  if (want <= 0) return want < 0 ? want : PULSAR_EINVAL;
+  if (n_parts != want) return PULSAR_EINVAL;
+  if (q_len > n_self || n_self > cap || cap < 8 || self_pos0 < 0) return PULSAR_EINVAL;
+  if (cap % 8 != 0) return PULSAR_EUNSUPPORTED;
+  if (!aligned16(qq) || !aligned16(o_part) || !lse_part || !aligned16(k_self_cache) ||
+      !aligned16(v_self_cache))
+    return PULSAR_EINVAL;
+  if (n_shards > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) return PULSAR_EINVAL;
+  if (n_shards > 0 && shard_len % 8 != 0) return PULSAR_EUNSUPPORTED;
+  if ((int64_t)batch * n_shards * shard_len * a->n_kv_heads > INT32_MAX) return PULSAR_EUNSUPPORTED;
+  if ((int64_t)batch * q_len > INT32_MAX / 2) return PULSAR_EUNSUPPORTED;
+  Phase2Geometry pg = phase2_geometry(batch, n_shards, n_shards > 0 ? shard_len : 1, q_len,
+                                      a->n_q_heads, a->n_kv_heads, a->head_dim, 1);
+  const Layout2 l = layout2(pg);
+  if (!ws || ws_bytes < l.k_rot) return PULSAR_EWORKSPACE;   // the rotated query only
+  if (!aligned16(ws)) return PULSAR_EINVAL;
+  uint16_t* q_rot = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + l.q_rot);
+  hipStream_t s = as_stream(stream);
+  // query token t is self token n_self - q_len + t
+  if (launch_phase2_prep(qq, nullptr, nullptr, batch, q_len, a->n_q_heads, a->n_kv_heads,
+                         a->head_dim, self_pos0 + n_self - q_len, a->rope_base, 8, q_rot, nullptr,
+                         nullptr, s))
+    return PULSAR_EHIP;
+  SelfShard self{};
+  self.k = k_self_cache;
+  self.v = v_self_cache;
+  self.k_seq = (int64_t)cap * a->n_kv_heads * a->head_dim;
+  self.v_seq = (int64_t)a->n_kv_heads * a->head_dim * cap;
+  self.n = n_self;
+  self.v_ld = cap;
+  return launch_phase2(pg, q_rot, k_cache, v_cache, self, o_part, lse_part, s) == 0 ? PULSAR_OK
+                                                                                       : PULSAR_EHIP;
 }
 
 int pulsar_lse_merge(int32_t batch, int32_t n_parts, int32_t q_len, int32_t n_q_heads,

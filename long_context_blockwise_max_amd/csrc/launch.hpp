@@ -53,11 +53,31 @@ Phase2Geometry phase2_geometry(int32_t batch, int32_t n_shards, int32_t shard_le
                                int32_t q_len, int32_t n_q_heads, int32_t n_kv_heads,
                                int32_t head_dim, int32_t has_self);
 
-// q_rot [B][Lq][Hq][d] and k_self_rot [B][Lq][Hkv][d] are already rotated;
-// v_self_t is the d-major copy [B][Hkv][d][self_pad] of the self values
+// The query host's own shard: n tokens (the Lq queries are the last Lq of them).
+// Keys rotated, token j of sequence b at k + b * k_seq + j * Hkv * d; values
+// d-major, the (b, head, d) row at v + b * v_seq + (head * d + d) * v_ld, with
+// columns n .. round_up(n, 8) - 1 finite.  k == nullptr: no self shard.
+struct SelfShard {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_seq, v_seq;
+  int32_t n, v_ld;
+};
+
+// q_rot [B][Lq][Hq][d] already rotated
 int launch_phase2(const Phase2Geometry& g, const uint16_t* q_rot, const uint16_t* k_cache,
-                  const uint16_t* v_cache, const uint16_t* k_self_rot, const uint16_t* v_self_t,
-                  float* o_part, float* lse_part, hipStream_t stream);
+                  const uint16_t* v_cache, const SelfShard& self, float* o_part,
+                  float* lse_part, hipStream_t stream);
+
+// Append n_new tokens to self caches of capacity cap holding n_self tokens:
+// k_new / v_new [B][n_new][Hkv][d] pre-RoPE, token j at position pos0 + n_self + j;
+// k_cache [B][cap][Hkv][d] receives the rotated keys, v_cache [B][Hkv][d][cap] the
+// values (d-major); columns past the last token up to the next multiple of 8 are
+// zeroed.
+int launch_self_append(const uint16_t* k_new, const uint16_t* v_new, int32_t batch,
+                       int32_t n_new, int32_t n_self, int32_t cap, int32_t n_kv_heads,
+                       int32_t head_dim, int64_t pos0, double rope_base, uint16_t* k_cache,
+                       uint16_t* v_cache, hipStream_t stream);
 
 int launch_merge(int32_t batch, int32_t n_parts, int32_t q_len, int32_t n_q_heads,
                  int32_t head_dim, const float* o_part, const float* lse_part, float* o,

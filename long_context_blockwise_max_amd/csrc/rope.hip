@@ -181,6 +181,52 @@ __global__ void __launch_bounds__(256) phase2_prep(const uint16_t* __restrict__ 
     }
 }
 
+// Self-cache append (generation): one workgroup per (sequence, new token).  The
+// first D/2 threads derive cos/sin of the token's position into LDS; the
+// workgroup rotates the token's Hkv key heads into the key cache and writes its
+// values into their d-major columns.  The workgroup of the last new token also
+// zeroes the value columns from the new length up to the next multiple of 8,
+// which the attention kernels read (masked) in runs of 8 keys.
+template <int D>
+__global__ void __launch_bounds__(256) self_append(const uint16_t* __restrict__ k_new,
+                                                   const uint16_t* __restrict__ v_new,
+                                                   int32_t n_new, int32_t n_self, int32_t cap,
+                                                   int32_t hkv, int64_t pos0, double base,
+                                                   uint16_t* __restrict__ kc,
+                                                   uint16_t* __restrict__ vc) {
+  constexpr int HALF = D / 2;
+  constexpr int CPH = HALF / 8;
+  __shared__ float cs_l[HALF], sn_l[HALF];
+  const int j = blockIdx.x % n_new;
+  const int bb = blockIdx.x / n_new;
+  const int slot = n_self + j;
+  if ((int)threadIdx.x < HALF)
+    rope_cos_sin(pos0 + slot, threadIdx.x, HALF, base, &cs_l[threadIdx.x], &sn_l[threadIdx.x]);
+  __syncthreads();
+  const uint16_t* ksrc = k_new + ((int64_t)bb * n_new + j) * hkv * D;
+  uint16_t* kdst = kc + ((int64_t)bb * cap + slot) * hkv * D;
+  for (int idx = threadIdx.x; idx < hkv * CPH; idx += blockDim.x) {
+    const int h = idx / CPH, c = idx % CPH;
+    float cs[8], sn[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      cs[e] = cs_l[8 * c + e];
+      sn[e] = sn_l[8 * c + e];
+    }
+    rotate_chunk<D>(ksrc + (int64_t)h * D, kdst + (int64_t)h * D, c, cs, sn);
+  }
+  const uint16_t* vsrc = v_new + ((int64_t)bb * n_new + j) * hkv * D;
+  uint16_t* vbase = vc + (int64_t)bb * hkv * D * cap;
+  for (int idx = threadIdx.x; idx < hkv * D; idx += blockDim.x)
+    vbase[(int64_t)idx * cap + slot] = vsrc[idx];
+  if (j == n_new - 1) {
+    const int n_tot = n_self + n_new;
+    const int pad = ((n_tot + 7) & ~7) - n_tot;
+    for (int idx = threadIdx.x; idx < hkv * D * pad; idx += blockDim.x)
+      vbase[(int64_t)(idx / pad) * cap + n_tot + idx % pad] = 0;
+  }
+}
+
 static int grid_for(int64_t n, int threads) {
   int64_t g = (n + threads - 1) / threads;
   if (g > 65536) g = 65536;
@@ -221,6 +267,20 @@ int launch_phase2_prep(const uint16_t* qq, const uint16_t* k_self, const uint16_
   else
     hipLaunchKernelGGL(phase2_prep<64>, grid, dim3(256), 0, stream, qq, k_self, v_self, q_len,
                        n_tok, n_q_heads, n_kv_heads, pos0, rope_base, lq_pad, q_rot, k_rot, v_t);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int launch_self_append(const uint16_t* k_new, const uint16_t* v_new, int32_t batch,
+                       int32_t n_new, int32_t n_self, int32_t cap, int32_t n_kv_heads,
+                       int32_t head_dim, int64_t pos0, double rope_base, uint16_t* k_cache,
+                       uint16_t* v_cache, hipStream_t stream) {
+  const dim3 grid((unsigned)(batch * n_new));
+  if (head_dim == 128)
+    hipLaunchKernelGGL(self_append<128>, grid, dim3(256), 0, stream, k_new, v_new, n_new, n_self,
+                       cap, n_kv_heads, pos0, rope_base, k_cache, v_cache);
+  else
+    hipLaunchKernelGGL(self_append<64>, grid, dim3(256), 0, stream, k_new, v_new, n_new, n_self,
+                       cap, n_kv_heads, pos0, rope_base, k_cache, v_cache);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

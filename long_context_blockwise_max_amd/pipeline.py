@@ -146,5 +146,50 @@ class HotPath:
         self.phase2(stream)
         self.merge(stream)
 
+    # generation ---------------------------------------------------------
+    def decode_setup(self, max_new: int):
+        """Self caches for the query tokens plus up to max_new generated tokens,
+        primed with the query tokens' own keys and values (self token 0 sits at
+        position L, right after the context)."""
+        g = self.geo
+        dev = self.device
+        hkv, hq, d = g.n_kv_heads, g.n_q_heads, g.head_dim
+        self.cap = (g.q_len + max_new + 63) // 64 * 64
+        self.k_self_cache = _bf16_empty((g.batch, self.cap, hkv, d), dev)
+        self.v_self_cache = _bf16_empty((g.batch, hkv, d, self.cap), dev)
+        self.n_self = 0
+        self.q1 = _bf16_empty((g.batch, 1, hq, d), dev)
+        self.k1 = _bf16_empty((g.batch, 1, hkv, d), dev)
+        self.v1 = _bf16_empty((g.batch, 1, hkv, d), dev)
+        self.n_parts1 = B.pulsar_phase2_num_parts(self.cattn, g.batch, g.n_blocks, g.block_size, 1, True)
+        self.o_part1 = torch.empty((g.batch, self.n_parts1, 1, hq, d), dtype=torch.float32, device=dev)
+        self.lse_part1 = torch.empty((g.batch, self.n_parts1, 1, hq), dtype=torch.float32, device=dev)
+        self.ws1 = torch.empty(max(B.pulsar_phase2_workspace_bytes(self.cattn, g.batch, 1, False), 256),
+                               dtype=torch.uint8, device=dev)
+        self.o1 = torch.empty((g.batch, 1, hq, d), dtype=torch.float32, device=dev)
+        self.lse1 = torch.empty((g.batch, 1, hq), dtype=torch.float32, device=dev)
+        self.self_append(self.k_self, self.v_self, g.q_len)
+
+    def self_append(self, k_new, v_new, n_new, stream=None):
+        g = self.geo
+        B.pulsar_self_append(self.cattn, g.batch, self.cap, self.n_self, n_new, g.context_len,
+                             k_new, v_new, self.k_self_cache, self.v_self_cache, stream)
+        self.n_self += n_new
+
+    def decode_step(self, q_new=None, k_new=None, v_new=None, stream=None):
+        """One generated token: append its key / value (default k1, v1), attend its
+        query (default q1) to every retained shard and the self cache, merge into
+        o1 / lse1.  Token tensors are [B][1][H][d] bf16 on the device."""
+        g = self.geo
+        q_new = self.q1 if q_new is None else q_new
+        self.self_append(self.k1 if k_new is None else k_new, self.v1 if v_new is None else v_new,
+                         1, stream)
+        B.pulsar_phase2_decode(self.cattn, g.batch, g.n_blocks, g.block_size, q_new, 1,
+                               self.k_cache, self.v_cache, self.k_self_cache, self.v_self_cache,
+                               self.cap, self.n_self, g.context_len, self.o_part1, self.lse_part1,
+                               self.n_parts1, self.ws1, stream)
+        B.pulsar_lse_merge(g.batch, self.n_parts1, 1, g.n_q_heads, g.head_dim, self.o_part1,
+                           self.lse_part1, self.o1, self.lse1, stream)
+
     def status_word(self) -> int:
         return int(self.ws[:4].view(torch.int32).item())

@@ -127,9 +127,10 @@ def retained_cache(k, v, n_blocks, block_size, base):
 
 
 # ----------------------------------------------------------------- Phase 2
-def _shard_attend(q_hat, k_hat, v, causal):
+def _shard_attend(q_hat, k_hat, v, causal, offset=0):
     """All query tokens against one shard.  q_hat [Lq][Hq][d], k_hat/v
-    [Hkv][n][d].  causal: query t sees shard keys 0..t.  -> O [Lq][Hq][d], lse [Lq][Hq]."""
+    [Hkv][n][d].  causal: query t sees shard keys 0..t+offset.
+    -> O [Lq][Hq][d], lse [Lq][Hq]."""
     lq, hq, d = q_hat.shape
     hkv, n, _ = k_hat.shape
     group = hq // hkv
@@ -139,7 +140,7 @@ def _shard_attend(q_hat, k_hat, v, causal):
         g = h // group
         s = q_hat[:, h, :] @ k_hat[g].T / np.sqrt(d)            # [Lq][n]
         if causal:
-            s = np.where(np.arange(n)[None, :] <= np.arange(lq)[:, None], s, -np.inf)
+            s = np.where(np.arange(n)[None, :] <= np.arange(lq)[:, None] + offset, s, -np.inf)
         m = s.max(axis=1, keepdims=True)
         w = np.exp(s - m)
         ws = w.sum(axis=1)
@@ -171,6 +172,67 @@ def phase2_partials(qq, q_pos0, k_cache, v_cache, k_self, v_self, base):
         vs = np.asarray(v_self, np.float64).transpose(1, 0, 2)
         parts.append(_shard_attend(q_hat, ks, vs, causal=True))
     return parts
+
+
+def decode_partials(qq, k_cache, v_cache, k_self, v_self, self_pos0, base):
+    """Phase 2 of a generation step.  The query host's own shard holds n_self
+    tokens at positions self_pos0 .. self_pos0 + n_self - 1: the query, then
+    every token generated so far ("Dropping the Anchor ..." Section 2.2; Section
+    5 runs the method with --tokens_to_generate 128).  The Lq query tokens are
+    the last Lq of them; query t attends to every retained shard and, causally,
+    to self tokens 0 .. n_self - Lq + t.
+
+    qq             [Lq][Hq][d] pre-RoPE
+    k_self, v_self [n_self][Hkv][d] pre-RoPE keys / values of the self tokens
+    returns per-part (O, lse) like phase2_partials, the self shard last.
+    With n_self == Lq this is phase2_partials with the self shard.
+    """
+    qq = np.asarray(qq, np.float64)
+    lq = qq.shape[0]
+    n_self = np.asarray(k_self).shape[0]
+    off = n_self - lq
+    q_hat = rotate_bf16(qq, self_pos0 + off + np.arange(lq), base)
+    parts = []
+    for s in range(k_cache.shape[0]):
+        parts.append(_shard_attend(q_hat, np.asarray(k_cache[s], np.float64),
+                                   np.asarray(v_cache[s], np.float64), causal=False))
+    ks = rotate_bf16(np.asarray(k_self, np.float64), self_pos0 + np.arange(n_self), base)
+    vs = np.asarray(v_self, np.float64)
+    parts.append(_shard_attend(q_hat, ks.transpose(1, 0, 2), vs.transpose(1, 0, 2), causal=True,
+                               offset=off))
+    return parts
+
+
+def dense_decode_attention(qq, k_cache, v_cache, k_self, v_self, self_pos0, base):
+    """Twin of decode_partials + lse_merge, written as one masked softmax per
+    query row over an explicit visible-key list."""
+    qq = np.asarray(qq, np.float64)
+    lq, hq, d = qq.shape
+    n_self = np.asarray(k_self).shape[0]
+    keys, vals = [], []
+    for s in range(k_cache.shape[0]):
+        keys.append(np.asarray(k_cache[s], np.float64))
+        vals.append(np.asarray(v_cache[s], np.float64))
+    ks = rotate_bf16(np.asarray(k_self, np.float64), self_pos0 + np.arange(n_self), base)
+    keys.append(ks.transpose(1, 0, 2))
+    vals.append(np.asarray(v_self, np.float64).transpose(1, 0, 2))
+    kc = np.concatenate(keys, axis=1)
+    vc = np.concatenate(vals, axis=1)
+    n_ret = kc.shape[1] - n_self
+    group = hq // kc.shape[0]
+    out = np.empty((lq, hq, d))
+    lse = np.empty((lq, hq))
+    for t in range(lq):
+        q_hat = rotate_bf16(qq[t:t + 1], np.array([self_pos0 + n_self - lq + t]), base)[0]
+        n_vis = n_ret + (n_self - lq + t + 1)      # retained keys, then self keys up to itself
+        for h in range(hq):
+            g = h // group
+            sc = kc[g, :n_vis] @ q_hat[h] / np.sqrt(d)
+            m = sc.max()
+            w = np.exp(sc - m)
+            out[t, h] = w @ vc[g, :n_vis] / w.sum()
+            lse[t, h] = m + np.log(w.sum())
+    return out, lse
 
 
 def lse_merge(o_parts, lse_parts):

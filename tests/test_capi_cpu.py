@@ -177,3 +177,32 @@ def test_merge_rejections_and_strerror():
     assert lib.pulsar_lse_merge(1, 4, 64, 32, 128, FAKE_MIS, FAKE, FAKE, None, None) == B.PULSAR_EINVAL
     for c in (0, -1, -2, -3, -4, 7):
         assert isinstance(B.strerror(c), str) and B.strerror(c)
+
+
+@needs_lib
+def test_generation_calls_reject_bad_arguments():
+    lib = B.lib()
+    A = ctypes.byref(ATTN)
+
+    def app(batch, cap, n_self, n_new, pos0=0, ptrs=None):
+        p = ptrs or [FAKE] * 4
+        return lib.pulsar_self_append(A, batch, cap, n_self, n_new, pos0, *p, None)
+
+    assert app(1, 64, 60, 5) == B.PULSAR_EINVAL            # past the capacity
+    assert app(1, 60, 0, 1) == B.PULSAR_EUNSUPPORTED       # capacity not a multiple of 8
+    assert app(0, 64, 0, 1) == B.PULSAR_EINVAL
+    assert app(1, 64, 0, 0) == B.PULSAR_EINVAL
+    assert app(1, 64, 0, 1, pos0=-1) == B.PULSAR_EINVAL
+    assert app(1, 64, 0, 1, ptrs=[FAKE, FAKE, FAKE_MIS, FAKE]) == B.PULSAR_EINVAL
+    n = B.pulsar_phase2_num_parts(ATTN, 1, 8, 16384, 1, True)
+    ws = B.pulsar_phase2_workspace_bytes(ATTN, 1, 1, False)
+
+    def dec(q_len, cap, n_self, n_parts=n, wsb=ws):
+        return lib.pulsar_phase2_decode(A, 1, 8, 16384, FAKE, q_len, FAKE, FAKE, FAKE, FAKE, cap,
+                                        n_self, 131072, FAKE, FAKE, n_parts, FAKE, wsb, None)
+
+    assert dec(1, 128, 65, n_parts=n + 1) == B.PULSAR_EINVAL
+    assert dec(1, 128, 129) == B.PULSAR_EINVAL             # more self tokens than the capacity
+    assert dec(1, 120, 0) == B.PULSAR_EINVAL               # fewer self tokens than queries
+    assert dec(1, 124, 65) == B.PULSAR_EUNSUPPORTED        # capacity not a multiple of 8
+    assert dec(1, 128, 65, wsb=ws - 1) == B.PULSAR_EWORKSPACE

@@ -1,0 +1,97 @@
+"""GPU parity of generation: self-cache append plus Phase-2 decode attention
+and merge, step by step, against the oracle's masked dense attention over the
+retained shards and the self tokens up to the new one."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as OA
+from tests.gpu_cases import LSE_ABS, Case, assert_close, log, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def _retained(case, seq):
+    w = case.w
+    if seq == 0:
+        khat = case.oracle_khat().astype(np.float64)
+        kc = khat.reshape(w.n_blocks, w.block_size, w.n_kv_heads, w.head_dim).transpose(0, 2, 1, 3)
+        vc = W.bf16_bits_to_f64(case.v).reshape(w.n_blocks, w.block_size, w.n_kv_heads, w.head_dim)
+        return kc, vc.transpose(0, 2, 1, 3)
+    return (W.bf16_bits_to_f64(W.extra_cache(w, seq, "k")),
+            W.bf16_bits_to_f64(W.extra_cache(w, seq, "v")))
+
+
+def _bits_to(dst, bits):
+    import torch
+    dst.copy_(torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+              .reshape(dst.shape))
+
+
+CASES = {
+    "tiny": {},
+    "decode_batch": dict(n_blocks=5, block_size=512, q_len=1, batch=3, n_planted=0),
+    "g4_d128": dict(n_blocks=2, block_size=640, n_q_heads=8, n_kv_heads=2, head_dim=128, q_len=5,
+                    budget_chunks=2, n_planted=0, batch=2),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_generation_steps_match_the_oracle(name):
+    torch = torch_cuda()
+    w = W.with_(W.CONFIGS["tiny"], name=name, **CASES[name])
+    n_gen = 3
+    case = Case(w)
+    case.run()
+    gq, gk, gv = W.generated(w, n_gen)
+    path = case.path
+    path.decode_setup(n_gen)
+    retained = [_retained(case, s) for s in range(w.batch)]
+    for step in range(n_gen):
+        _bits_to(path.q1, gq[step])
+        _bits_to(path.k1, gk[step])
+        _bits_to(path.v1, gv[step])
+        log(f"[decode] {name}: step {step} (self tokens {w.q_len + step + 1})")
+        path.decode_step()
+        torch.cuda.synchronize()
+        o = path.o1.cpu().numpy()
+        lse = path.lse1.cpu().numpy()
+        for s in range(w.batch):
+            ks = np.concatenate([case.kq[s], gk[:step + 1, s, 0]], axis=0)
+            vs = np.concatenate([case.vq[s], gv[:step + 1, s, 0]], axis=0)
+            kc, vc = retained[s]
+            want_o, want_lse = OA.dense_decode_attention(
+                W.bf16_bits_to_f64(gq[step, s]), kc, vc, W.bf16_bits_to_f64(ks),
+                W.bf16_bits_to_f64(vs), w.context_len, w.rope_base)
+            assert_close(o[s], want_o, f"{name} decode step {step} seq {s} O")
+            assert_close(lse[s], want_lse, f"{name} decode step {step} seq {s} LSE",
+                         max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+def test_decode_of_the_query_tokens_is_the_query_phase():
+    """With the self cache holding exactly the query tokens, decode attention of
+    those tokens is the query phase with its self shard."""
+    torch = torch_cuda()
+    from long_context_blockwise_max_amd import binding as B
+    w = W.with_(W.CONFIGS["tiny"], name="consistency", **CASES["g4_d128"])
+    case = Case(w)
+    case.run()
+    path = case.path
+    path.decode_setup(0)
+    g = path.geo
+    o_part = torch.empty_like(path.o_part)
+    lse_part = torch.empty_like(path.lse_part)
+    ws = torch.empty(B.pulsar_phase2_workspace_bytes(path.cattn, g.batch, g.q_len, False),
+                     dtype=torch.uint8, device="cuda")
+    B.pulsar_phase2_decode(path.cattn, g.batch, g.n_blocks, g.block_size, path.qq, g.q_len,
+                           path.k_cache, path.v_cache, path.k_self_cache, path.v_self_cache,
+                           path.cap, path.n_self, g.context_len, o_part, lse_part, path.n_parts, ws)
+    o = torch.empty_like(path.o_q)
+    lse = torch.empty_like(path.lse_q)
+    B.pulsar_lse_merge(g.batch, path.n_parts, g.q_len, g.n_q_heads, g.head_dim, o_part, lse_part,
+                       o, lse)
+    torch.cuda.synchronize()
+    assert_close(o.cpu().numpy(), path.o_q.cpu().numpy().astype(np.float64), "decode == query O",
+                 max_abs=1e-5, mean_abs=1e-6)
+    assert_close(lse.cpu().numpy(), path.lse_q.cpu().numpy().astype(np.float64), "decode == query LSE",
+                 max_abs=1e-5, mean_abs=1e-6)

@@ -203,3 +203,49 @@ def test_retained_cache_does_not_depend_on_selection():
     assert kc.shape == (N, 2, b, d)
     np.testing.assert_array_equal(vc[1, 0], v[b:, 0])
     np.testing.assert_array_equal(kc[1, 1, 3], A.rotate_bf16(k[b + 3:b + 4], [b + 3], base)[0, 1])
+
+
+def _decode_case(seed, n_shards=2, n=24, hq=4, hkv=2, d=16, n_self=7, lq=3):
+    rng = np.random.default_rng(seed)
+    kc = round_bf16(rng.standard_normal((n_shards, hkv, n, d)))
+    vc = round_bf16(rng.standard_normal((n_shards, hkv, n, d)))
+    qq = round_bf16(rng.standard_normal((lq, hq, d)))
+    ks = round_bf16(rng.standard_normal((n_self, hkv, d)))
+    vs = round_bf16(rng.standard_normal((n_self, hkv, d)))
+    return qq, kc, vc, ks, vs
+
+
+@pytest.mark.parametrize("n_self,lq", [(7, 3), (5, 1), (1, 1), (4, 4)])
+def test_decode_merge_equals_masked_dense_attention(n_self, lq):
+    qq, kc, vc, ks, vs = _decode_case(11 + n_self, n_self=n_self, lq=lq)
+    parts = A.decode_partials(qq, kc, vc, ks, vs, 1000, 1e4)
+    o, lse = A.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+    o2, lse2 = A.dense_decode_attention(qq, kc, vc, ks, vs, 1000, 1e4)
+    np.testing.assert_allclose(o, o2, atol=1e-12)
+    np.testing.assert_allclose(lse, lse2, atol=1e-12)
+
+
+def test_decode_with_self_equal_to_query_is_the_query_phase():
+    qq, kc, vc, ks, vs = _decode_case(5, n_self=3, lq=3)
+    a = A.decode_partials(qq, kc, vc, ks, vs, 500, 1e4)
+    b = A.phase2_partials(qq, 500, kc, vc, ks, vs, 1e4)
+    for (oa, la), (ob, lb) in zip(a, b):
+        np.testing.assert_allclose(oa, ob, atol=1e-13)
+        np.testing.assert_allclose(la, lb, atol=1e-13)
+
+
+def test_decode_zero_keys_average_exactly_the_visible_values():
+    # zero keys: every visible key scores 0, so each query row averages the
+    # values it may see: all retained ones and self tokens up to itself
+    qq, kc, vc, ks, vs = _decode_case(9, n_self=6, lq=2)
+    kc = np.zeros_like(kc)
+    ks = np.zeros_like(ks)
+    o, lse = A.dense_decode_attention(qq, kc, vc, ks, vs, 40, 1e4)
+    n_ret = kc.shape[0] * kc.shape[2]
+    for t in range(2):
+        n_vis_self = 6 - 2 + t + 1
+        for h in range(qq.shape[1]):
+            g = h // 2
+            want = (vc[:, g].reshape(-1, vc.shape[-1]).sum(0) + vs[:n_vis_self, g].sum(0)) / (n_ret + n_vis_self)
+            np.testing.assert_allclose(o[t, h], want, atol=1e-12)
+            assert abs(lse[t, h] - np.log(n_ret + n_vis_self)) < 1e-12

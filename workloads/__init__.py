@@ -246,3 +246,14 @@ def filler_planted_tokens(seed: int, n_blocks: int, block_size: int, chunk: int,
 
 def with_(w: Workload, **kw) -> Workload:
     return replace(w, **kw)
+
+
+def generated(w: Workload, n_tokens: int):
+    """Tokens generated after the query (one per decode step), pre-RoPE bf16 bits:
+    q [n][B][1][Hq][d], k [n][B][1][Hkv][d], v [n][B][1][Hkv][d].  Drawn from a
+    seed sequence of their own, so the other tensors do not change with n."""
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, 0x6E6]))
+    q = _normal_bf16(rng, (n_tokens, w.batch, 1, w.n_q_heads, w.head_dim))
+    k = _normal_bf16(rng, (n_tokens, w.batch, 1, w.n_kv_heads, w.head_dim))
+    v = _normal_bf16(rng, (n_tokens, w.batch, 1, w.n_kv_heads, w.head_dim))
+    return q, k, v
