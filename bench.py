@@ -72,6 +72,31 @@ def recorded_traffic(workload, kernel):
     return None if ent is None else ent.get("bytes_per_launch")
 
 
+def prefix_rows(path, w, stream, reps=3):
+    """The prefix rows of every host in one pass over the last block's prefix
+    (after the main steps, which leave the caches and lists in place)."""
+    import numpy as np
+    import torch
+
+    from long_context_blockwise_max_amd import costs as C
+
+    n = path.prefix_rows()
+    torch.cuda.synchronize()
+    if n <= 0:
+        return {"rows": 0}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for j in range(reps):
+        path.prefix_rows()
+        ev[j + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev[j].elapsed_time(ev[j + 1]) for j in range(reps)]))
+    flop = C.prefix_rows_flops(n, w.n_q_heads, w.head_dim)
+    return {"rows": n, "ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flop": flop}
+
+
 def generation(path, w, n_tokens, stream):
     """Generated tokens after the query: each step appends the token's key and
     value to the query host's self cache, attends its query to every retained
@@ -288,6 +313,7 @@ def main():
                             "unit": "GB/s", "frac": round(p2_gbs / PEAK_HBM_GBS, 4),
                             "traffic": recorded_traffic(w.name, "phase2_kernel")},
     }
+    out["prefix_rows"] = prefix_rows(path, w, stream)
     if args.gen_tokens > 0:
         out["generation"] = generation(path, w, args.gen_tokens, stream)
     if not args.no_cpu_baseline:

@@ -144,6 +144,24 @@ int pulsar_phase1_attend(const pulsar_geom* g, const pulsar_attn* a, const uint1
                          const uint16_t* v_cache, float* o, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* Prefix rows.  In the method each host runs one forward pass over
+ * [prefix_i || B_i] ("Dropping the Anchor ..." Section 2; the Dutch technical
+ * summary writes the input as [S_sink || Sigma_0 || ... || Sigma_{i-1} || B_i]),
+ * so its prefix rows are queries too; their outputs are what a next layer needs.
+ * Every host's prefix is a leading part of the last block's prefix, so one pass
+ * over that list gives them all: list entry e (a position p_e, duplicates kept)
+ * attends to entries 0 .. e, at original positions.
+ * pulsar_prefix_rows_len: the number of rows, sink_size + chunk_size * kept *
+ * (n_blocks - 1) for n_blocks >= 2, else 0 (-1 for an invalid geometry).
+ * pulsar_phase1_prefix_rows writes o_prefix [rows][Hq][d] float32, row e the
+ * output of list entry e; it reads what pulsar_phase1_prepare left in k_cache,
+ * v_cache and ws (same geometry, same stream) and does nothing for 0 rows.
+ * Errors: as pulsar_phase1_encode. */
+int64_t pulsar_prefix_rows_len(const pulsar_geom* g);
+int pulsar_phase1_prefix_rows(const pulsar_geom* g, const pulsar_attn* a,
+                              const uint16_t* k_cache, const uint16_t* v_cache, float* o_prefix,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* Number of partial results pulsar_phase2_query writes per sequence for this
  * shape: every shard is split into the same number of contiguous key ranges,
  * plus one part for the self shard when has_self != 0.  Returns <= 0 on error. */

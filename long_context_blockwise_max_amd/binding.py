@@ -23,6 +23,7 @@ PULSAR_EUNSUPPORTED = -4
 EXPORTED = (
     "pulsar_workspace_bytes", "pulsar_kept_chunks", "pulsar_select", "pulsar_phase1_encode",
     "pulsar_phase1_prepare", "pulsar_phase1_attend", "pulsar_self_append", "pulsar_phase2_decode",
+    "pulsar_prefix_rows_len", "pulsar_phase1_prefix_rows",
     "pulsar_phase2_num_parts", "pulsar_phase2_workspace_bytes", "pulsar_phase2_query",
     "pulsar_lse_merge", "pulsar_strerror",
 )
@@ -77,6 +78,10 @@ def lib():
         L.pulsar_phase2_query.argtypes = [A, i32, i32, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp,
                                           i32, vp, sz, vp]
         L.pulsar_phase2_query.restype = ctypes.c_int
+        L.pulsar_prefix_rows_len.argtypes = [G]
+        L.pulsar_prefix_rows_len.restype = i64
+        L.pulsar_phase1_prefix_rows.argtypes = [G, A, vp, vp, vp, vp, sz, vp]
+        L.pulsar_phase1_prefix_rows.restype = ctypes.c_int
         L.pulsar_self_append.argtypes = [A, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp]
         L.pulsar_self_append.restype = ctypes.c_int
         L.pulsar_phase2_decode.argtypes = [A, i32, i32, i32, vp, i32, vp, vp, vp, vp, i32, i32, i64,
@@ -238,6 +243,23 @@ def pulsar_phase2_query(attn: Attn, batch, n_shards, shard_len, qq, q_len, q_pos
         _ptr(o_part, torch.float32, rows * d, "o_part"), _ptr(lse_part, torch.float32, rows, "lse_part"),
         n_parts, _ptr(ws, torch.uint8, 0, "ws"), ws.numel(), _stream(stream))
     _check(rc, "pulsar_phase2_query")
+
+
+def pulsar_prefix_rows_len(geom: Geom) -> int:
+    return lib().pulsar_prefix_rows_len(ctypes.byref(geom))
+
+
+def pulsar_phase1_prefix_rows(geom: Geom, attn: Attn, k_cache, v_cache, o_prefix, ws, stream=None):
+    import torch
+    L = geom.n_blocks * geom.block_size
+    hq, hkv, d = attn.n_q_heads, attn.n_kv_heads, attn.head_dim
+    n = pulsar_prefix_rows_len(geom)
+    rc = lib().pulsar_phase1_prefix_rows(
+        ctypes.byref(geom), ctypes.byref(attn), _bf16(k_cache, L * hkv * d, "k_cache"),
+        _bf16(v_cache, L * hkv * d, "v_cache"),
+        _ptr(o_prefix, torch.float32, max(n, 0) * hq * d, "o_prefix", allow_none=n <= 0),
+        _ptr(ws, torch.uint8, 0, "ws"), ws.numel(), _stream(stream))
+    _check(rc, "pulsar_phase1_prefix_rows")
 
 
 def pulsar_self_append(attn: Attn, batch, cap, n_self, n_new, self_pos0, k_new, v_new,

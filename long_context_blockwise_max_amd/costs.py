@@ -86,3 +86,8 @@ def phase2_kernel_bytes(batch, n_shards, shard_len, q_len, n_q_heads, n_kv_heads
     K/V, query, self K/V, merged output); split-KV partials are overhead on top."""
     return phase2_bytes(batch, n_shards, shard_len, q_len, n_q_heads, n_kv_heads, head_dim,
                         with_self)
+
+
+def prefix_rows_flops(n_rows, n_q_heads, head_dim) -> float:
+    """Prefix rows: list entry e attends to entries 0..e, 4 d Hq FLOPs per pair."""
+    return 4.0 * head_dim * n_q_heads * n_rows * (n_rows + 1) / 2

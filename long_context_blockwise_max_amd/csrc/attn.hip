@@ -384,24 +384,38 @@ struct P1Args {
   const int32_t* krow;     // prefix index lists
   const int32_t* vcol;
   const int32_t* order;    // [N * n_rt] (block, row tile) pairs, longest first
-  float* o;                // [L][Hq][D]
+  float* o;                // [L][Hq][D] (prefix rows: [P][Hq][D])
   int32_t n_blocks, b, chunk, kept, sink, hq, hkv, group, hpw, n_hs, n_rt, rpw;
   float scale_log2;
 };
 
-template <int D>
+// PR = false: the block rows of every block (the encode step).
+// PR = true: the prefix rows.  The last block's prefix list
+// [sink || summaries of blocks 0 .. N-2] is itself a sequence: its entry e is a
+// query at its original position and attends to entries 0 .. e (every host's
+// prefix is a leading part of this list, so one pass serves all hosts).  Tiles
+// come through the list, the mask is causal in list order, row tiles run longest
+// first, and a.n_rt counts the list's row tiles.
+
+template <int D, bool PR>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NTHR, NTHR), amdgpu_waves_per_eu(2, 2)))
 phase1_kernel(P1Args a) {
   constexpr int NQ = 1;
   __shared__ __attribute__((aligned(1024))) char smem[2 * Stage<D>::BYTES];
 
   const int hc_count = a.hkv * a.n_hs;
-  const int pair = a.order[blockIdx.x / hc_count];
   const int hc = blockIdx.x % hc_count;
   const int g = hc % a.hkv;
   const int hs = hc / a.hkv;
-  const int i = pair / a.n_rt;
-  const int rt = pair % a.n_rt;
+  int i, rt;
+  if constexpr (PR) {
+    i = a.n_blocks - 1;
+    rt = a.n_rt - 1 - (int)(blockIdx.x / hc_count);   // longest row tiles first
+  } else {
+    const int pair = a.order[blockIdx.x / hc_count];
+    i = pair / a.n_rt;
+    rt = pair % a.n_rt;
+  }
   const int wave = threadIdx.x >> 6;
   const int lr = threadIdx.x & 31;
   const int h = g * a.group + hs * a.hpw + (wave % a.hpw);
@@ -409,8 +423,9 @@ phase1_kernel(P1Args a) {
 
   const int span = a.chunk * a.kept;
   const int P = (i == 0) ? 0 : a.sink + span * i;
-  const int n_pre = (P + KT - 1) / KT;
-  const int own_end = min((rt + 1) * a.rpw, a.b);
+  const int n_rows = PR ? P : a.b;                  // query rows of the sequence
+  const int n_pre = PR ? 0 : (P + KT - 1) / KT;     // list tiles seen in full
+  const int own_end = min((rt + 1) * a.rpw, n_rows);
   const int n_own = (own_end + KT - 1) / KT;
   const int n_tiles = n_pre + n_own;
   const int64_t lst = p1_list_start(i, a.sink, span);
@@ -427,7 +442,14 @@ phase1_kernel(P1Args a) {
   bf16x8 qf[NQ][D / 16];
   {
     const int r = r0 + lr;
-    load_q<D>(r < a.b ? a.q + (((int64_t)i * a.b + r) * a.hq + h) * D : nullptr, qf[0]);
+    int64_t pos = (int64_t)i * a.b + r;
+    if constexpr (PR) {
+      // position of list entry r: its K row is blk * Hkv * b + w, position blk * b + w
+      const int64_t kr = r < n_rows ? krow[r] : 0;
+      const int64_t hb = (int64_t)a.hkv * a.b;
+      pos = (kr / hb) * a.b + kr % hb;
+    }
+    load_q<D>(r < n_rows ? a.q + (pos * a.hq + h) * D : nullptr, qf[0]);
   }
 
   FlashState<D, NQ> st;
@@ -440,7 +462,18 @@ phase1_kernel(P1Args a) {
   constexpr int KNI = KTile<D>::NI, VNI = VTile<D>::NI;
   int32_t rk[KNI], rv[VNI];
   auto fetch_raw = [&](int t) __attribute__((always_inline)) {
-    if (t < n_pre) {
+    if (PR) {   // every tile through the list, entries past this tile's rows clamped
+#pragma unroll
+      for (int x = 0; x < KNI; ++x) {
+        const int e = t * KT + staged_k_row<D>(x);
+        rk[x] = krow[e < own_end ? e : 0];
+      }
+#pragma unroll
+      for (int x = 0; x < VNI; ++x) {
+        const int e = t * KT + 8 * staged_v_chunk<D>(x);
+        rv[x] = vcol[e < own_end ? e : 0];
+      }
+    } else if (t < n_pre) {
 #pragma unroll
       for (int x = 0; x < KNI; ++x) {
         const int e = t * KT + staged_k_row<D>(x);
@@ -466,7 +499,7 @@ phase1_kernel(P1Args a) {
   };
   auto src_of = [&](int t) __attribute__((always_inline)) {
     TileSrc<D> sr;
-    const bool pre = t < n_pre;
+    const bool pre = PR || t < n_pre;
 #pragma unroll
     for (int x = 0; x < KNI; ++x) sr.k[x] = ((pre ? kb_ : own_k) + rk[x]) * D;
 #pragma unroll
@@ -495,8 +528,8 @@ phase1_kernel(P1Args a) {
   }
 
   const int r = r0 + lr;
-  flash_finish<D, NQ>(st, 0, r < a.b ? a.o + (((int64_t)i * a.b + r) * a.hq + h) * D : nullptr,
-                      nullptr);
+  const int64_t orow = PR ? (int64_t)r : (int64_t)i * a.b + r;
+  flash_finish<D, NQ>(st, 0, r < n_rows ? a.o + (orow * a.hq + h) * D : nullptr, nullptr);
 }
 
 // Work order: (block, row tile) pairs by descending number of key tiles, ties by
@@ -614,9 +647,48 @@ int launch_phase1_attend(const Phase1Geometry& g, const uint16_t* q_rot, const u
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.head_dim));
   const int grid = n_pairs * g.n_kv_heads * g.n_head_sub;
   if (g.head_dim == 128)
-    hipLaunchKernelGGL(phase1_kernel<128>, dim3(grid), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL((phase1_kernel<128, false>), dim3(grid), dim3(NTHR), 0, stream, a);
   else
-    hipLaunchKernelGGL(phase1_kernel<64>, dim3(grid), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL((phase1_kernel<64, false>), dim3(grid), dim3(NTHR), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int64_t phase1_prefix_rows_len(const Phase1Geometry& g) {
+  return g.n_blocks < 2 ? 0 : (int64_t)g.sink_size + (int64_t)g.chunk_size * g.kept * (g.n_blocks - 1);
+}
+
+int launch_phase1_prefix_rows(const Phase1Geometry& g, const uint16_t* q_rot,
+                              const uint16_t* k_cache, const uint16_t* v_cache,
+                              const int32_t* prefix_rows, float* o_prefix, hipStream_t stream) {
+  const int64_t n = phase1_prefix_rows_len(g);
+  if (n == 0) return 0;
+  const int64_t total = phase1_prefix_total(g);
+  P1Args a;
+  a.q = q_rot;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.krow = prefix_rows;
+  a.vcol = prefix_rows + total;
+  a.order = nullptr;
+  a.o = o_prefix;
+  a.n_blocks = g.n_blocks;
+  a.b = g.block_size;
+  a.chunk = g.chunk_size;
+  a.kept = g.kept;
+  a.sink = g.sink_size;
+  a.hq = g.n_q_heads;
+  a.hkv = g.n_kv_heads;
+  a.group = g.n_q_heads / g.n_kv_heads;
+  a.hpw = g.heads_per_wg;
+  a.n_hs = g.n_head_sub;
+  a.rpw = g.rows_per_wg;
+  a.n_rt = (int32_t)((n + g.rows_per_wg - 1) / g.rows_per_wg);
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.head_dim));
+  const int grid = a.n_rt * g.n_kv_heads * g.n_head_sub;
+  if (g.head_dim == 128)
+    hipLaunchKernelGGL((phase1_kernel<128, true>), dim3(grid), dim3(NTHR), 0, stream, a);
+  else
+    hipLaunchKernelGGL((phase1_kernel<64, true>), dim3(grid), dim3(NTHR), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

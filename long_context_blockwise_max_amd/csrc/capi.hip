@@ -247,6 +247,27 @@ int pulsar_phase1_encode(const pulsar_geom* g, const pulsar_attn* a, const uint1
              : PULSAR_OK;
 }
 
+int64_t pulsar_prefix_rows_len(const pulsar_geom* g) {
+  if (check_geom(g) != PULSAR_OK) return -1;
+  Phase1Geometry pg = phase1_geometry(g->n_blocks, g->block_size, g->chunk_size, kept_chunks(g),
+                                      g->sink_size, 1, 1, 64);
+  return phase1_prefix_rows_len(pg);
+}
+
+int pulsar_phase1_prefix_rows(const pulsar_geom* g, const pulsar_attn* a,
+                              const uint16_t* k_cache, const uint16_t* v_cache, float* o_prefix,
+                              void* ws, size_t ws_bytes, void* stream) {
+  P1Ws w;
+  int rc = phase1_common(g, a, k_cache, v_cache, ws, ws_bytes, &w);
+  if (rc) return rc;
+  if (phase1_prefix_rows_len(w.pg) == 0) return PULSAR_OK;
+  if (!aligned16(o_prefix)) return PULSAR_EINVAL;
+  return launch_phase1_prefix_rows(w.pg, w.q_rot, k_cache, v_cache, w.lists, o_prefix,
+                                   as_stream(stream))
+             ? PULSAR_EHIP
+             : PULSAR_OK;
+}
+
 int32_t pulsar_phase2_num_parts(const pulsar_attn* a, int32_t batch, int32_t n_shards,
                                 int32_t shard_len, int32_t q_len, int32_t has_self) {
   if (check_attn(a) != PULSAR_OK) return PULSAR_EINVAL;

@@ -45,6 +45,15 @@ int launch_phase1_attend(const Phase1Geometry& g, const uint16_t* q_rot, const u
                          const uint16_t* v_cache, const int32_t* prefix_rows,
                          const int32_t* order, float* o, hipStream_t stream);
 
+// number of prefix rows: the last block's prefix length (0 for one block)
+int64_t phase1_prefix_rows_len(const Phase1Geometry& g);
+
+// attention output of every prefix row, o_prefix [P][Hq][d]; reads what
+// launch_rope_fill and launch_phase1_lists wrote
+int launch_phase1_prefix_rows(const Phase1Geometry& g, const uint16_t* q_rot,
+                              const uint16_t* k_cache, const uint16_t* v_cache,
+                              const int32_t* prefix_rows, float* o_prefix, hipStream_t stream);
+
 struct Phase2Geometry {
   int32_t batch, n_shards, shard_len, q_len, n_q_heads, n_kv_heads, head_dim;
   int32_t has_self, nq, n_row_groups, splits, n_parts, self_pad;

@@ -146,6 +146,18 @@ class HotPath:
         self.phase2(stream)
         self.merge(stream)
 
+    def prefix_rows(self, stream=None):
+        """Attention output of every prefix row into o_prefix [rows][Hq][d]
+        (after phase1_prepare / phase1)."""
+        g = self.geo
+        n = B.pulsar_prefix_rows_len(self.cgeom)
+        if getattr(self, "o_prefix", None) is None or self.o_prefix.shape[0] != max(n, 1):
+            self.o_prefix = torch.empty((max(n, 1), g.n_q_heads, g.head_dim), dtype=torch.float32,
+                                        device=self.device)
+        B.pulsar_phase1_prefix_rows(self.cgeom, self.cattn, self.k_cache[0], self.v_cache[0],
+                                    self.o_prefix if n > 0 else None, self.ws, stream)
+        return n
+
     # generation ---------------------------------------------------------
     def decode_setup(self, max_new: int):
         """Self caches for the query tokens plus up to max_new generated tokens,

@@ -114,6 +114,58 @@ def phase1_block_dense(q, k_hat, v, prefix_i, i, block_size, base):
     return out
 
 
+def prefix_rows(q, k_hat, v, prefix_last, rows, base):
+    """Attention output of prefix rows, the states a next layer would need.
+    Host i runs one forward pass over [prefix_i || B_i]; its prefix rows are
+    queries too, each attending causally (by list index) to the prefix entries up
+    to itself ("Dropping the Anchor ..." Section 2 and the Dutch technical
+    summary's per-host input [S_sink || Sigma_0 || ... || Sigma_{i-1} || B_i]).
+    Every prefix_i is a leading part of the last block's prefix, so one pass
+    over prefix_last gives every host's prefix rows.
+
+    q, k_hat, v : indexable [L][H][d] (q pre-RoPE, k_hat rotated bf16)
+    prefix_last : positions of the last block's prefix (duplicates kept)
+    rows        : list indices e; row e attends to prefix_last[0 .. e]
+    returns O [len(rows)][Hq][d]
+    """
+    prefix_last = np.asarray(prefix_last, np.int64)
+    outs = []
+    for e in rows:
+        keys = prefix_last[:e + 1]
+        p = prefix_last[e]
+        q_hat = rotate_bf16(np.asarray(q[np.array([p])], np.float64), np.array([p]), base)[0]
+        o, _ = attend(q_hat, k_hat[keys], v[keys])
+        outs.append(o)
+    return np.stack(outs)
+
+
+def prefix_rows_dense(q, k_hat, v, prefix_last, base):
+    """Twin of prefix_rows for every row: one softmax per row over all context
+    positions with bias ln(multiplicity of the position among entries 0..e) and
+    -inf where the position does not occur."""
+    q = np.asarray(q, np.float64)
+    k_hat = np.asarray(k_hat, np.float64)
+    v = np.asarray(v, np.float64)
+    prefix_last = np.asarray(prefix_last, np.int64)
+    n_ctx = int(prefix_last.max()) + 1
+    hq, d = q.shape[1], q.shape[2]
+    group = hq // k_hat.shape[1]
+    out = np.empty((len(prefix_last), hq, d))
+    counts = np.zeros(n_ctx)
+    for e, p in enumerate(prefix_last):
+        counts[p] += 1
+        with np.errstate(divide="ignore"):
+            bias = np.log(counts)
+        q_hat = rotate_bf16(q[np.array([p])], np.array([p]), base)[0]
+        for h in range(hq):
+            g = h // group
+            s = k_hat[:n_ctx, g, :] @ q_hat[h] / np.sqrt(d) + bias
+            m = s.max()
+            w = np.exp(s - m)
+            out[e, h] = w @ v[:n_ctx, g, :] / w.sum()
+    return out
+
+
 def retained_cache(k, v, n_blocks, block_size, base):
     """What each host keeps after Phase 1: its own block's rotated keys and its
     values, [N][Hkv][b][d] each.  Sink and summary entries are discarded."""

@@ -249,3 +249,37 @@ def test_decode_zero_keys_average_exactly_the_visible_values():
             want = (vc[:, g].reshape(-1, vc.shape[-1]).sum(0) + vs[:n_vis_self, g].sum(0)) / (n_ret + n_vis_self)
             np.testing.assert_allclose(o[t, h], want, atol=1e-12)
             assert abs(lse[t, h] - np.log(n_ret + n_vis_self)) < 1e-12
+
+
+def _prefix_case(seed, L=96, hq=4, hkv=2, d=16):
+    rng = np.random.default_rng(seed)
+    q = round_bf16(rng.standard_normal((L, hq, d)))
+    k = round_bf16(rng.standard_normal((L, hkv, d)))
+    v = round_bf16(rng.standard_normal((L, hkv, d)))
+    khat = A.rotate_bf16(k, np.arange(L), 1e4)
+    return q, khat, v
+
+
+def test_prefix_rows_of_a_contiguous_prefix_are_textbook_causal_attention():
+    # Star setting: the prefix is block 0 itself, so its rows are plain causal
+    # attention over block 0 (float64 softmax of QK^T/sqrt(d) with a causal mask)
+    q, khat, v = _prefix_case(3)
+    n = 40
+    got = A.prefix_rows(q, khat, v, np.arange(n), range(n), 1e4)
+    qh = A.rotate_bf16(q[:n], np.arange(n), 1e4)
+    for h in range(q.shape[1]):
+        g = h // 2
+        s = qh[:, h, :] @ khat[:n, g, :].T / math.sqrt(q.shape[2])
+        s = np.where(np.tril(np.ones((n, n), bool)), s, -np.inf)
+        want = torch.softmax(torch.from_numpy(s), dim=1).numpy() @ v[:n, g, :]
+        np.testing.assert_allclose(got[:, h, :], want, atol=1e-12)
+
+
+def test_prefix_rows_gather_equals_multiplicity_bias_dense():
+    # a sink of 16 positions followed by chunks of 8, one of them inside the sink
+    # (kept twice, as the method's prefix does)
+    q, khat, v = _prefix_case(7)
+    pre = np.concatenate([np.arange(16), np.arange(8, 16), np.arange(40, 48), np.arange(72, 80)])
+    got = A.prefix_rows(q, khat, v, pre, range(len(pre)), 1e4)
+    want = A.prefix_rows_dense(q, khat, v, pre, 1e4)
+    np.testing.assert_allclose(got, want, atol=1e-12)
