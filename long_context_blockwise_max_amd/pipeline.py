@@ -188,10 +188,11 @@ class HotPath:
                              k_new, v_new, self.k_self_cache, self.v_self_cache, stream)
         self.n_self += n_new
 
-    def decode_step(self, q_new=None, k_new=None, v_new=None, stream=None):
+    def decode_step(self, q_new=None, k_new=None, v_new=None, o_out=None, stream=None):
         """One generated token: append its key / value (default k1, v1), attend its
         query (default q1) to every retained shard and the self cache, merge into
-        o1 / lse1.  Token tensors are [B][1][H][d] bf16 on the device."""
+        o_out (default o1, with its LSE in lse1).  Token tensors are [B][1][H][d]
+        bf16 on the device."""
         g = self.geo
         q_new = self.q1 if q_new is None else q_new
         self.self_append(self.k1 if k_new is None else k_new, self.v1 if v_new is None else v_new,
@@ -201,7 +202,30 @@ class HotPath:
                                self.cap, self.n_self, g.context_len, self.o_part1, self.lse_part1,
                                self.n_parts1, self.ws1, stream)
         B.pulsar_lse_merge(g.batch, self.n_parts1, 1, g.n_q_heads, g.head_dim, self.o_part1,
-                           self.lse_part1, self.o1, self.lse1, stream)
+                           self.lse_part1, self.o1 if o_out is None else o_out,
+                           self.lse1 if o_out is None else None, stream)
+
+    def capture_generation(self, q_new, k_new, v_new):
+        """Capture n generation steps (self cache primed anew, then one step per
+        token; q_new / k_new / v_new [n][B][1][H][d] on the device) into one HIP
+        graph.  Every step's arguments, the self-cache length included, are fixed
+        at capture, so a replay recomputes the same n steps into
+        o_steps [n][B][1][Hq][d].  Only this library's kernels are captured (no memsets,
+        no allocations)."""
+        g = self.geo
+        n = q_new.shape[0]
+        self.decode_setup(n)
+        self.o_steps = torch.empty((n, g.batch, 1, g.n_q_heads, g.head_dim), dtype=torch.float32,
+                                   device=self.device)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        with torch.cuda.graph(graph, stream=side):
+            self.n_self = 0
+            self.self_append(self.k_self, self.v_self, g.q_len)
+            for j in range(n):
+                self.decode_step(q_new[j], k_new[j], v_new[j], o_out=self.o_steps[j])
+        return graph
 
     def status_word(self) -> int:
         return int(self.ws[:4].view(torch.int32).item())
