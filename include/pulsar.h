@@ -67,13 +67,17 @@ typedef struct pulsar_geom {
 } pulsar_geom;
 
 /* Attention geometry.  head_dim 64 or 128; n_q_heads = G * n_kv_heads with the
- * group size G in {1, 2, 4} or a multiple of 8; L * n_kv_heads * head_dim < 2^31. */
+ * group size G in {1, 2, 4} or a multiple of 8; L * n_kv_heads * head_dim < 2^31.
+ * rope_scaling: 0 plain RoPE; 1 the Llama-3.1 frequency scaling (factor 8, low-
+ * and high-frequency factors 1 and 4, original context 8192: frequencies with a
+ * wavelength under 2048 positions kept, over 8192 divided by 8, blended between),
+ * for use with Llama-3.1 weights. */
 typedef struct pulsar_attn {
   int32_t n_q_heads;
   int32_t n_kv_heads;
   int32_t head_dim;
-  int32_t reserved;   /* must be 0 */
-  double rope_base;   /* > 1, e.g. 500000 */
+  int32_t rope_scaling;   /* 0 or 1 */
+  double rope_base;       /* > 1, e.g. 500000 */
 } pulsar_attn;
 
 /* Bytes of workspace pulsar_select and pulsar_phase1_encode need for this

@@ -43,7 +43,7 @@ class Geom(ctypes.Structure):
 
 class Attn(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rope_scaling", ctypes.c_int32),
                 ("rope_base", ctypes.c_double)]
 
 
@@ -103,8 +103,8 @@ def make_geom(n_blocks, block_size, chunk_size, budget_chunks, sink_size, vocab_
     return Geom(n_blocks, block_size, chunk_size, budget_chunks, sink_size, vocab_size)
 
 
-def make_attn(n_q_heads, n_kv_heads, head_dim, rope_base) -> Attn:
-    return Attn(n_q_heads, n_kv_heads, head_dim, 0, float(rope_base))
+def make_attn(n_q_heads, n_kv_heads, head_dim, rope_base, rope_scaling=0) -> Attn:
+    return Attn(n_q_heads, n_kv_heads, head_dim, int(rope_scaling), float(rope_base))
 
 
 # ----------------------------------------------------------------- helpers

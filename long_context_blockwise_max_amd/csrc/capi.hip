@@ -45,7 +45,8 @@ int check_geom(const pulsar_geom* g) {
 
 int check_attn(const pulsar_attn* a) {
   if (!a) return PULSAR_EINVAL;
-  if (a->n_q_heads < 1 || a->n_kv_heads < 1 || a->reserved != 0) return PULSAR_EINVAL;
+  if (a->n_q_heads < 1 || a->n_kv_heads < 1) return PULSAR_EINVAL;
+  if (a->rope_scaling != 0 && a->rope_scaling != 1) return PULSAR_EINVAL;
   if (a->n_q_heads % a->n_kv_heads != 0) return PULSAR_EINVAL;
   if (!(a->rope_base > 1.0) || !isfinite(a->rope_base)) return PULSAR_EINVAL;
   if (a->head_dim != 64 && a->head_dim != 128) return PULSAR_EUNSUPPORTED;
@@ -187,7 +188,7 @@ int phase1_prepare_checked(const pulsar_geom* g, const pulsar_attn* a, const uin
                            uint16_t* k_cache, uint16_t* v_cache, const P1Ws& w, hipStream_t s) {
   const int64_t L = (int64_t)g->n_blocks * g->block_size;
   if (launch_rope_fill(q, k, v, L, g->block_size, a->n_q_heads, a->n_kv_heads, a->head_dim,
-                       a->rope_base, w.q_rot, k_cache, v_cache, s))
+                       a->rope_base, a->rope_scaling, w.q_rot, k_cache, v_cache, s))
     return PULSAR_EHIP;
   if (launch_phase1_lists(w.pg, sel, w.lists, w.order, s)) return PULSAR_EHIP;
   return PULSAR_OK;
@@ -314,7 +315,7 @@ int pulsar_phase2_query(const pulsar_attn* a, int32_t batch, int32_t n_shards, i
   hipStream_t s = as_stream(stream);
   if ((int64_t)batch * q_len > INT32_MAX / 2) return PULSAR_EUNSUPPORTED;
   if (launch_phase2_prep(qq, has_self ? k_self : nullptr, v_self, batch, q_len, a->n_q_heads,
-                         a->n_kv_heads, a->head_dim, q_pos0, a->rope_base, pg.self_pad, q_rot,
+                         a->n_kv_heads, a->head_dim, q_pos0, a->rope_base, a->rope_scaling, pg.self_pad, q_rot,
                          k_rot, v_t, s))
     return PULSAR_EHIP;
   SelfShard self{};
@@ -342,7 +343,7 @@ int pulsar_self_append(const pulsar_attn* a, int32_t batch, int32_t cap, int32_t
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_self_cache) || !aligned16(v_self_cache))
     return PULSAR_EINVAL;
   return launch_self_append(k_new, v_new, batch, n_new, n_self, cap, a->n_kv_heads, a->head_dim,
-                            self_pos0, a->rope_base, k_self_cache, v_self_cache,
+                            self_pos0, a->rope_base, a->rope_scaling, k_self_cache, v_self_cache,
                             as_stream(stream)) == 0
              ? PULSAR_OK
              : PULSAR_EHIP;
@@ -375,7 +376,8 @@ int pulsar_phase2_decode(const pulsar_attn* a, int32_t batch, int32_t n_shards,
   hipStream_t s = as_stream(stream);
   // query token t is self token n_self - q_len + t
   if (launch_phase2_prep(qq, nullptr, nullptr, batch, q_len, a->n_q_heads, a->n_kv_heads,
-                         a->head_dim, self_pos0 + n_self - q_len, a->rope_base, 8, q_rot, nullptr,
+                         a->head_dim, self_pos0 + n_self - q_len, a->rope_base, a->rope_scaling, 8, q_rot,
+                         nullptr,
                          nullptr, s))
     return PULSAR_EHIP;
   SelfShard self{};

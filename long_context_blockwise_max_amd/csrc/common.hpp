@@ -31,9 +31,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // Rotary angle pair for position `pos` and frequency index i (of half = d/2):
 // theta = pos * base^(-i/half) in float64, cos/sin in float64, rounded to float32.
+// Llama-3.1 frequency scaling (the "llama3" rope type published with Llama 3.1:
+// factor 8, low-frequency factor 1, high-frequency factor 4, original context
+// 8192): frequencies whose wavelength 2 pi / f is under 8192 / 4 positions are
+// kept, those over 8192 / 1 are divided by 8, and in between the two are blended
+// linearly in 8192 / wavelength.
+__device__ __forceinline__ double llama3_scale(double inv) {
+  constexpr double kFactor = 8.0, kLow = 1.0, kHigh = 4.0, kOrig = 8192.0;
+  const double wavelen = 6.283185307179586 / inv;
+  if (wavelen < kOrig / kHigh) return inv;
+  if (wavelen > kOrig / kLow) return inv / kFactor;
+  const double smooth = (kOrig / wavelen - kLow) / (kHigh - kLow);
+  return (1.0 - smooth) * inv / kFactor + smooth * inv;
+}
+
+// scaling: 0 none, 1 Llama-3.1
 __device__ __forceinline__ void rope_cos_sin(int64_t pos, int i, int half, double base,
-                                             float* c, float* s) {
+                                             int scaling, float* c, float* s) {
   double inv = pow(base, -(double)i / (double)half);
+  if (scaling == 1) inv = llama3_scale(inv);
   double th = (double)pos * inv;
   double sd, cd;
   sincos(th, &sd, &cd);

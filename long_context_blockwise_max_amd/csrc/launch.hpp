@@ -12,16 +12,17 @@ int launch_select(const int32_t* tok, int32_t n_blocks, int32_t block_size, int3
 
 int launch_rope_fill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t L,
                      int32_t block_size, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                     double rope_base, uint16_t* q_rot, uint16_t* k_cache, uint16_t* v_cache,
-                     hipStream_t stream);
+                     double rope_base, int32_t scaling, uint16_t* q_rot, uint16_t* k_cache,
+                     uint16_t* v_cache, hipStream_t stream);
 
 // Phase-2 prep: q_rot [B][Lq][Hq][d] and k_rot [B][Lq][Hkv][d] rotated at positions
 // pos0 + t; v_t the d-major self values [B][Hkv][d][lq_pad].  k_self == NULL: no self shard
 // (k_rot, v_self and v_t unused)
 int launch_phase2_prep(const uint16_t* qq, const uint16_t* k_self, const uint16_t* v_self,
                        int32_t batch, int32_t q_len, int32_t n_q_heads, int32_t n_kv_heads,
-                       int32_t head_dim, int64_t pos0, double rope_base, int32_t lq_pad,
-                       uint16_t* q_rot, uint16_t* k_rot, uint16_t* v_t, hipStream_t stream);
+                       int32_t head_dim, int64_t pos0, double rope_base, int32_t scaling,
+                       int32_t lq_pad, uint16_t* q_rot, uint16_t* k_rot, uint16_t* v_t,
+                       hipStream_t stream);
 
 struct Phase1Geometry {
   int32_t n_blocks, block_size, chunk_size, kept, sink_size;
@@ -85,8 +86,8 @@ int launch_phase2(const Phase2Geometry& g, const uint16_t* q_rot, const uint16_t
 // zeroed.
 int launch_self_append(const uint16_t* k_new, const uint16_t* v_new, int32_t batch,
                        int32_t n_new, int32_t n_self, int32_t cap, int32_t n_kv_heads,
-                       int32_t head_dim, int64_t pos0, double rope_base, uint16_t* k_cache,
-                       uint16_t* v_cache, hipStream_t stream);
+                       int32_t head_dim, int64_t pos0, double rope_base, int32_t scaling,
+                       uint16_t* k_cache, uint16_t* v_cache, hipStream_t stream);
 
 int launch_merge(int32_t batch, int32_t n_parts, int32_t q_len, int32_t n_q_heads,
                  int32_t head_dim, const float* o_part, const float* lse_part, float* o,

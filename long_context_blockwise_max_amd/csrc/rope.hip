@@ -25,10 +25,10 @@
 namespace pulsar {
 
 template <int D>
-__device__ __forceinline__ void chunk_angles(int64_t pos, int c, double base, float (&cs)[8],
-                                             float (&sn)[8]) {
+__device__ __forceinline__ void chunk_angles(int64_t pos, int c, double base, int scaling,
+                                             float (&cs)[8], float (&sn)[8]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) rope_cos_sin(pos, 8 * c + e, D / 2, base, &cs[e], &sn[e]);
+  for (int e = 0; e < 8; ++e) rope_cos_sin(pos, 8 * c + e, D / 2, base, scaling, &cs[e], &sn[e]);
 }
 
 template <int D>
@@ -54,7 +54,8 @@ template <int D>
 __global__ void __launch_bounds__(256) rope_fill(const uint16_t* __restrict__ q,
                                                  const uint16_t* __restrict__ k, int64_t L,
                                                  int32_t block_size, int32_t n_q, int32_t n_kv,
-                                                 double base, uint16_t* __restrict__ q_rot,
+                                                 double base, int32_t scaling,
+                                                 uint16_t* __restrict__ q_rot,
                                                  uint16_t* __restrict__ kc) {
   constexpr int HALF = D / 2;
   constexpr int CPH = HALF / 8;  // pair chunks per head row
@@ -64,7 +65,7 @@ __global__ void __launch_bounds__(256) rope_fill(const uint16_t* __restrict__ q,
     const int c = (int)(idx % CPH);
     const int64_t pos = idx / CPH;
     float cs[8], sn[8];
-    chunk_angles<D>(pos, c, base, cs, sn);
+    chunk_angles<D>(pos, c, base, scaling, cs, sn);
     for (int h = 0; h < n_q; ++h) {
       const int64_t r = (pos * n_q + h) * D;
       rotate_chunk<D>(q + r, q_rot + r, c, cs, sn);
@@ -130,7 +131,8 @@ __global__ void __launch_bounds__(256) phase2_prep(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ ks,
                                                    const uint16_t* __restrict__ vs, int32_t lq,
                                                    int32_t n_tok, int32_t hq, int32_t hkv,
-                                                   int64_t pos0, double base, int32_t lq_pad,
+                                                   int64_t pos0, double base, int32_t scaling,
+                                                   int32_t lq_pad,
                                                    uint16_t* __restrict__ q_rot,
                                                    uint16_t* __restrict__ k_rot,
                                                    uint16_t* __restrict__ vt) {
@@ -140,8 +142,8 @@ __global__ void __launch_bounds__(256) phase2_prep(const uint16_t* __restrict__ 
     __shared__ float cs_l[HALF], sn_l[HALF];
     const int t = blockIdx.x;
     const int64_t pos = pos0 + t % lq;
-    if ((int)threadIdx.x < HALF) rope_cos_sin(pos, threadIdx.x, HALF, base, &cs_l[threadIdx.x],
-                                              &sn_l[threadIdx.x]);
+    if ((int)threadIdx.x < HALF)
+      rope_cos_sin(pos, threadIdx.x, HALF, base, scaling, &cs_l[threadIdx.x], &sn_l[threadIdx.x]);
     __syncthreads();
     const int n_heads = hq + (ks ? hkv : 0);
     for (int idx = threadIdx.x; idx < n_heads * CPH; idx += blockDim.x) {
@@ -192,7 +194,7 @@ __global__ void __launch_bounds__(256) self_append(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ v_new,
                                                    int32_t n_new, int32_t n_self, int32_t cap,
                                                    int32_t hkv, int64_t pos0, double base,
-                                                   uint16_t* __restrict__ kc,
+                                                   int32_t scaling, uint16_t* __restrict__ kc,
                                                    uint16_t* __restrict__ vc) {
   constexpr int HALF = D / 2;
   constexpr int CPH = HALF / 8;
@@ -201,7 +203,7 @@ __global__ void __launch_bounds__(256) self_append(const uint16_t* __restrict__ 
   const int bb = blockIdx.x / n_new;
   const int slot = n_self + j;
   if ((int)threadIdx.x < HALF)
-    rope_cos_sin(pos0 + slot, threadIdx.x, HALF, base, &cs_l[threadIdx.x], &sn_l[threadIdx.x]);
+    rope_cos_sin(pos0 + slot, threadIdx.x, HALF, base, scaling, &cs_l[threadIdx.x], &sn_l[threadIdx.x]);
   __syncthreads();
   const uint16_t* ksrc = k_new + ((int64_t)bb * n_new + j) * hkv * D;
   uint16_t* kdst = kc + ((int64_t)bb * cap + slot) * hkv * D;
@@ -236,18 +238,18 @@ static int grid_for(int64_t n, int threads) {
 
 int launch_rope_fill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t L,
                      int32_t block_size, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                     double rope_base, uint16_t* q_rot, uint16_t* k_cache, uint16_t* v_cache,
-                     hipStream_t stream) {
+                     double rope_base, int32_t scaling, uint16_t* q_rot, uint16_t* k_cache,
+                     uint16_t* v_cache, hipStream_t stream) {
   const int64_t n = L * (head_dim / 16);
   const dim3 tgrid((unsigned)((L + 63) / 64), (unsigned)n_kv_heads);
   if (head_dim == 128) {
     hipLaunchKernelGGL(rope_fill<128>, dim3(grid_for(n, 256)), dim3(256), 0, stream, q, k, L,
-                       block_size, n_q_heads, n_kv_heads, rope_base, q_rot, k_cache);
+                       block_size, n_q_heads, n_kv_heads, rope_base, scaling, q_rot, k_cache);
     hipLaunchKernelGGL(v_cache_fill<128>, tgrid, dim3(256), 0, stream, v, L, block_size,
                        n_kv_heads, v_cache);
   } else {
     hipLaunchKernelGGL(rope_fill<64>, dim3(grid_for(n, 256)), dim3(256), 0, stream, q, k, L,
-                       block_size, n_q_heads, n_kv_heads, rope_base, q_rot, k_cache);
+                       block_size, n_q_heads, n_kv_heads, rope_base, scaling, q_rot, k_cache);
     hipLaunchKernelGGL(v_cache_fill<64>, tgrid, dim3(256), 0, stream, v, L, block_size,
                        n_kv_heads, v_cache);
   }
@@ -256,31 +258,34 @@ int launch_rope_fill(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
 
 int launch_phase2_prep(const uint16_t* qq, const uint16_t* k_self, const uint16_t* v_self,
                        int32_t batch, int32_t q_len, int32_t n_q_heads, int32_t n_kv_heads,
-                       int32_t head_dim, int64_t pos0, double rope_base, int32_t lq_pad,
-                       uint16_t* q_rot, uint16_t* k_rot, uint16_t* v_t, hipStream_t stream) {
+                       int32_t head_dim, int64_t pos0, double rope_base, int32_t scaling,
+                       int32_t lq_pad, uint16_t* q_rot, uint16_t* k_rot, uint16_t* v_t,
+                       hipStream_t stream) {
   const int32_t n_tok = batch * q_len;
   const int32_t n_vt = k_self ? ((q_len + 63) / 64) * n_kv_heads * batch : 0;
   const dim3 grid((unsigned)(n_tok + n_vt));
   if (head_dim == 128)
     hipLaunchKernelGGL(phase2_prep<128>, grid, dim3(256), 0, stream, qq, k_self, v_self, q_len,
-                       n_tok, n_q_heads, n_kv_heads, pos0, rope_base, lq_pad, q_rot, k_rot, v_t);
+                       n_tok, n_q_heads, n_kv_heads, pos0, rope_base, scaling, lq_pad, q_rot, k_rot,
+                       v_t);
   else
     hipLaunchKernelGGL(phase2_prep<64>, grid, dim3(256), 0, stream, qq, k_self, v_self, q_len,
-                       n_tok, n_q_heads, n_kv_heads, pos0, rope_base, lq_pad, q_rot, k_rot, v_t);
+                       n_tok, n_q_heads, n_kv_heads, pos0, rope_base, scaling, lq_pad, q_rot, k_rot,
+                       v_t);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 int launch_self_append(const uint16_t* k_new, const uint16_t* v_new, int32_t batch,
                        int32_t n_new, int32_t n_self, int32_t cap, int32_t n_kv_heads,
-                       int32_t head_dim, int64_t pos0, double rope_base, uint16_t* k_cache,
-                       uint16_t* v_cache, hipStream_t stream) {
+                       int32_t head_dim, int64_t pos0, double rope_base, int32_t scaling,
+                       uint16_t* k_cache, uint16_t* v_cache, hipStream_t stream) {
   const dim3 grid((unsigned)(batch * n_new));
   if (head_dim == 128)
     hipLaunchKernelGGL(self_append<128>, grid, dim3(256), 0, stream, k_new, v_new, n_new, n_self,
-                       cap, n_kv_heads, pos0, rope_base, k_cache, v_cache);
+                       cap, n_kv_heads, pos0, rope_base, scaling, k_cache, v_cache);
   else
     hipLaunchKernelGGL(self_append<64>, grid, dim3(256), 0, stream, k_new, v_new, n_new, n_self,
-                       cap, n_kv_heads, pos0, rope_base, k_cache, v_cache);
+                       cap, n_kv_heads, pos0, rope_base, scaling, k_cache, v_cache);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -30,6 +30,7 @@ class Geometry:
     batch: int = 1
     rope_base: float = 500000.0
     with_self: bool = True
+    rope_scaling: int = 0      # 1: Llama-3.1 frequency scaling
 
     @property
     def context_len(self):
@@ -53,7 +54,7 @@ class HotPath:
         L, hq, hkv, d = g.context_len, g.n_q_heads, g.n_kv_heads, g.head_dim
         self.cgeom = B.make_geom(g.n_blocks, g.block_size, g.chunk_size, g.budget_chunks,
                                  g.sink_size, g.vocab_size)
-        self.cattn = B.make_attn(hq, hkv, d, g.rope_base)
+        self.cattn = B.make_attn(hq, hkv, d, g.rope_base, g.rope_scaling)
         self.kept = B.pulsar_kept_chunks(self.cgeom)
         if self.kept < 0:
             raise B.PulsarError(B.PULSAR_EINVAL, "geometry")

@@ -31,11 +31,17 @@ def torch_cuda():
     return torch
 
 
+def rope_spec(w: W.Workload):
+    """The RoPE base as the oracle takes it (marked when the workload scales)."""
+    from oracle.rope import Llama3Base
+    return Llama3Base(w.rope_base) if w.rope_scaling == 1 else w.rope_base
+
+
 def geometry_of(w: W.Workload, with_self=True):
     from long_context_blockwise_max_amd.pipeline import Geometry
     return Geometry(w.n_blocks, w.block_size, w.chunk_size, w.budget_chunks, w.sink_size,
                     w.vocab_size, w.n_q_heads, w.n_kv_heads, w.head_dim, w.q_len, w.batch,
-                    w.rope_base, with_self)
+                    w.rope_base, with_self, w.rope_scaling)
 
 
 class Case:
@@ -80,7 +86,7 @@ class Case:
         step = 8192
         for s in range(0, w.context_len, step):
             kb = W.bf16_bits_to_f64(self.k[s:s + step])
-            out[s:s + step] = OA.rotate_bf16(kb, np.arange(s, s + kb.shape[0]), w.rope_base)
+            out[s:s + step] = OA.rotate_bf16(kb, np.arange(s, s + kb.shape[0]), rope_spec(w))
         return out
 
 

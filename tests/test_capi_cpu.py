@@ -101,7 +101,7 @@ def test_phase1_rejects_bad_arguments():
     assert call(g, B.make_attn(24, 8, 128, 5e5), args, ws) == B.PULSAR_EUNSUPPORTED  # group of 3
     assert call(g, B.make_attn(32, 8, 128, 1.0), args, ws) == B.PULSAR_EINVAL
     bad = B.make_attn(32, 8, 128, 5e5)
-    bad.reserved = 1
+    bad.rope_scaling = 2
     assert call(g, bad, args, ws) == B.PULSAR_EINVAL
     for i in range(7):
         p = list(args)

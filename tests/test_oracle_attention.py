@@ -283,3 +283,27 @@ def test_prefix_rows_gather_equals_multiplicity_bias_dense():
     got = A.prefix_rows(q, khat, v, pre, range(len(pre)), 1e4)
     want = A.prefix_rows_dense(q, khat, v, pre, 1e4)
     np.testing.assert_allclose(got, want, atol=1e-12)
+
+
+# ------------------------------------------------------ Llama-3.1 scaling
+def test_llama3_scaling_regimes_at_base_500000_d128():
+    # wavelength 2 pi * 500000^(i/64): below 2048 for i <= 28, above 8192 for i >= 35
+    from oracle.rope import Llama3Base, inv_freq
+    plain = inv_freq(128, 500000.0)
+    scaled = inv_freq(128, Llama3Base(500000.0))
+    assert np.array_equal(scaled[:29], plain[:29])
+    np.testing.assert_allclose(scaled[35:], plain[35:] / 8.0, rtol=1e-15)
+    mid = scaled[29:35] / plain[29:35]
+    assert np.all((mid > 1.0 / 8.0) & (mid < 1.0)) and np.all(np.diff(mid) < 0)
+
+
+def test_llama3_scaled_low_frequencies_rotate_as_one_eighth_of_the_position():
+    from oracle.rope import Llama3Base
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((5, 2, 128))
+    pos = np.array([0, 8, 800, 8000, 131072])
+    a = rope(x, pos, Llama3Base(500000.0))
+    b = rope(x, pos // 8, 500000.0)
+    for i in range(35, 64):   # the low-frequency pairs (i, i + 64)
+        np.testing.assert_allclose(a[..., [i, i + 64]], b[..., [i, i + 64]], atol=1e-12)
+    np.testing.assert_allclose(a[..., :29], rope(x, pos, 500000.0)[..., :29], atol=1e-12)

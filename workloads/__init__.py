@@ -47,6 +47,7 @@ class Workload:
     batch: int
     rope_base: float = 500000.0
     zipf_s: float = 1.1
+    rope_scaling: int = 0      # 1: Llama-3.1 frequency scaling
 
     @property
     def context_len(self) -> int:
