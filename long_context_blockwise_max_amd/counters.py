@@ -30,6 +30,11 @@ COPY_MARK = "neg_kernel"
 
 
 def short_name(full: str) -> str:
+    # the second template argument tells the forms of the attention kernels apart
+    if "phase1_kernel" in full and ", true>" in full:
+        return "phase1_kernel_prefix_rows"
+    if "phase2_kernel" in full and ", true>" in full:
+        return "phase2_kernel_decode"
     for k in KERNELS:
         if k in full:
             return k

@@ -24,7 +24,7 @@ def _csv(path, counter, rows):
 
 def test_summary_scales_by_copy_and_gates_on_source(tmp_path):
     copy = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>(...)"
-    p1 = "void pulsar::phase1_kernel<128>(pulsar::P1Args)"
+    p1 = "void pulsar::phase1_kernel<128, false>(pulsar::P1Args)"
     # copy of 1 MiB reads 1024 KiB reported as 512 + 512; phase1 twice
     _csv(tmp_path / "f.csv", "FETCH_SIZE", [(1, copy, [512.0, 512.0]), (2, p1, [1000.0, 1000.0]),
                                              (3, p1, [1500.0, 1500.0])])
@@ -41,3 +41,9 @@ def test_summary_scales_by_copy_and_gates_on_source(tmp_path):
     assert e["write_bytes"] == 200 * 1024 * 2       # write scale 2.0
     assert rec["source_hash"] == bench.kernel_source_hash()
     assert "phase1_kernel" in md.read_text()
+
+
+def test_template_forms_are_told_apart():
+    assert counters.short_name("void pulsar::phase1_kernel<128, false>(pulsar::P1Args)") == "phase1_kernel"
+    assert counters.short_name("void pulsar::phase1_kernel<128, true>(pulsar::P1Args)") == "phase1_kernel_prefix_rows"
+    assert counters.short_name("void pulsar::phase2_kernel<64, true>(pulsar::P2Args)") == "phase2_kernel_decode"
