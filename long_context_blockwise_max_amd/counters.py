@@ -24,8 +24,9 @@ import json
 import os
 import sys
 
-KERNELS = ("phase1_kernel", "phase2_kernel", "rope_fill", "phase1_prefix_list", "phase1_order",
-           "select_df", "select_topk", "lse_merge_kernel", "rope_rows", "v_self_fill")
+KERNELS = ("phase1_kernel", "phase2_kernel", "phase2_prep", "rope_fill", "v_cache_fill",
+           "phase1_prefix_list", "phase1_order", "select_clear", "select_df", "select_topk",
+           "lse_merge_kernel", "self_append")
 COPY_MARK = "neg_kernel"
 
 
