@@ -245,7 +245,9 @@ int pulsar_phase2_decode(const pulsar_attn* a, int32_t batch, int32_t n_shards,
  *   lse = ln sum_p exp(lse_part[p]),  o = sum_p exp(lse_part[p] - lse) * o_part[p]
  *   o_part [B][n_parts][Lq][Hq][d] float32, lse_part [B][n_parts][Lq][Hq] float32
  *   o      [B][Lq][Hq][d] float32 out, lse [B][Lq][Hq] float32 out (may be NULL)
- * Errors: PULSAR_EINVAL, PULSAR_EHIP. */
+ * Errors: PULSAR_EINVAL (a size below 1, a null or misaligned pointer),
+ * PULSAR_EUNSUPPORTED (d other than 64 or 128, Lq * Hq above 2^31 - 1, or
+ * B * Lq * Hq above 4 (2^31 - 1)), PULSAR_EHIP. */
 int pulsar_lse_merge(int32_t batch, int32_t n_parts, int32_t q_len, int32_t n_q_heads,
                      int32_t head_dim, const float* o_part, const float* lse_part, float* o,
                      float* lse, void* stream);

@@ -114,6 +114,17 @@ Layout2 layout2(const Phase2Geometry& pg) {
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// one workgroup per (sequence, KV head, row group, part); a launch takes at most
+// 2^31 - 1 workgroups
+bool phase2_grid_ok(const Phase2Geometry& pg) {
+  if ((int64_t)pg.batch * pg.n_kv_heads * pg.n_row_groups * pg.n_parts > INT32_MAX) return false;
+  // the preparation launch: one workgroup per query token, plus one per 64 self
+  // tokens of each sequence and KV head for the value transpose
+  const int64_t tok = (int64_t)pg.batch * pg.q_len;
+  const int64_t vt = pg.has_self ? (int64_t)((pg.q_len + 63) / 64) * pg.n_kv_heads * pg.batch : 0;
+  return tok + vt <= INT32_MAX;
+}
+
 }  // namespace
 
 extern "C" {
@@ -305,6 +316,7 @@ int pulsar_phase2_query(const pulsar_attn* a, int32_t batch, int32_t n_shards, i
   if ((int64_t)batch * n_shards * shard_len * a->n_kv_heads > INT32_MAX) return PULSAR_EUNSUPPORTED;
   Phase2Geometry pg = phase2_geometry(batch, n_shards, n_shards > 0 ? shard_len : 1, q_len,
                                       a->n_q_heads, a->n_kv_heads, a->head_dim, has_self);
+  if (!phase2_grid_ok(pg)) return PULSAR_EUNSUPPORTED;
   const Layout2 l = layout2(pg);
   if (!ws || ws_bytes < l.total) return PULSAR_EWORKSPACE;
   if (!aligned16(ws)) return PULSAR_EINVAL;
@@ -369,6 +381,7 @@ int pulsar_phase2_decode(const pulsar_attn* a, int32_t batch, int32_t n_shards,
   if ((int64_t)batch * q_len > INT32_MAX / 2) return PULSAR_EUNSUPPORTED;
   Phase2Geometry pg = phase2_geometry(batch, n_shards, n_shards > 0 ? shard_len : 1, q_len,
                                       a->n_q_heads, a->n_kv_heads, a->head_dim, 1);
+  if (!phase2_grid_ok(pg)) return PULSAR_EUNSUPPORTED;
   const Layout2 l = layout2(pg);
   if (!ws || ws_bytes < l.k_rot) return PULSAR_EWORKSPACE;   // the rotated query only
   if (!aligned16(ws)) return PULSAR_EINVAL;
@@ -397,6 +410,9 @@ int pulsar_lse_merge(int32_t batch, int32_t n_parts, int32_t q_len, int32_t n_q_
   if (batch < 1 || n_parts < 1 || q_len < 1 || n_q_heads < 1) return PULSAR_EINVAL;
   if (head_dim != 64 && head_dim != 128) return PULSAR_EUNSUPPORTED;
   if (!aligned16(o_part) || !lse_part || !aligned16(o)) return PULSAR_EINVAL;
+  // rows of one sequence are counted in 32 bits; one wave per row, four rows a workgroup
+  if ((int64_t)q_len * n_q_heads > INT32_MAX) return PULSAR_EUNSUPPORTED;
+  if ((int64_t)batch * q_len * n_q_heads > (int64_t)INT32_MAX * 4) return PULSAR_EUNSUPPORTED;
   return launch_merge(batch, n_parts, q_len, n_q_heads, head_dim, o_part, lse_part, o, lse,
                       as_stream(stream)) == 0
              ? PULSAR_OK

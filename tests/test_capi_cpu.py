@@ -164,6 +164,13 @@ def test_phase2_part_count_and_rejections():
               None) == B.PULSAR_EINVAL                # negative position
     assert q2(1, 8, 16384, FAKE, 64, 131072, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, FAKE, ws2 - 1,
               None) == B.PULSAR_EWORKSPACE
+    # a query so long that the grid would pass 2^31 - 1 workgroups
+    # (4 sequences x 8 KV heads x 2^20 row groups x 64 parts = 2^31)
+    big_q = 1 << 26
+    n_big = B.pulsar_phase2_num_parts(ATTN, 4, 64, 64, big_q, False)
+    assert n_big == 64
+    assert q2(4, 64, 64, FAKE, big_q, 131072, FAKE, FAKE, None, None, FAKE, FAKE, n_big, FAKE,
+              1 << 62, None) == B.PULSAR_EUNSUPPORTED
     n_odd = B.pulsar_phase2_num_parts(ATTN, 1, 8, 1001, 64, True)
     assert q2(1, 8, 1001, FAKE, 64, 131072, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n_odd, FAKE, ws2,
               None) == B.PULSAR_EUNSUPPORTED          # shard length not a multiple of 8
@@ -175,6 +182,10 @@ def test_merge_rejections_and_strerror():
     assert lib.pulsar_lse_merge(0, 4, 64, 32, 128, FAKE, FAKE, FAKE, None, None) == B.PULSAR_EINVAL
     assert lib.pulsar_lse_merge(1, 4, 64, 32, 96, FAKE, FAKE, FAKE, None, None) == B.PULSAR_EUNSUPPORTED
     assert lib.pulsar_lse_merge(1, 4, 64, 32, 128, FAKE_MIS, FAKE, FAKE, None, None) == B.PULSAR_EINVAL
+    # sizes whose row counts or grid would not fit the launch
+    assert lib.pulsar_lse_merge(1, 4, 1 << 26, 64, 128, FAKE, FAKE, FAKE, None, None) == B.PULSAR_EUNSUPPORTED
+    assert lib.pulsar_lse_merge(1 << 10, 4, 1 << 20, 32, 128, FAKE, FAKE, FAKE, None,
+                                None) == B.PULSAR_EUNSUPPORTED
     for c in (0, -1, -2, -3, -4, 7):
         assert isinstance(B.strerror(c), str) and B.strerror(c)
 
