@@ -77,6 +77,17 @@ SMALL = {
     "single_block": dict(n_blocks=1, block_size=448, n_planted=0, budget_chunks=4),
     "star_small": dict(n_blocks=4, block_size=256, sink_size=256, budget_chunks=0, n_planted=0),
     "sink96_odd": dict(n_blocks=4, block_size=192, sink_size=96, budget_chunks=1, n_planted=0),
+    # no sink: block i > 0 sees only the summaries of earlier blocks
+    "no_sink": dict(n_blocks=3, block_size=256, sink_size=0, budget_chunks=2, n_planted=0),
+    # 16-token chunks; a block of 5.5 key tiles ends on a half tile
+    "ragged_352_chunk16": dict(n_blocks=3, block_size=352, chunk_size=16, budget_chunks=5,
+                               n_planted=0),
+    # 16 query heads on one KV head: two head groups per workgroup row tile
+    "g16_d64": dict(n_blocks=2, block_size=192, n_q_heads=16, n_kv_heads=1, budget_chunks=1,
+                    n_planted=0),
+    # budget above the chunk count: every chunk kept, so the sink tokens appear
+    # twice in the prefix (once as the sink, once inside block 0's summary)
+    "keep_all": dict(n_blocks=3, block_size=128, budget_chunks=100, n_planted=0),
 }
 
 

@@ -55,6 +55,10 @@ SMALL = {
                               q_len=1, batch=2, budget_chunks=1, n_planted=0),
     "decode_rows32": dict(n_blocks=3, block_size=256, n_q_heads=8, n_kv_heads=2, q_len=8,
                           budget_chunks=2, n_planted=0),
+    "g16_lq3": dict(n_blocks=2, block_size=256, n_q_heads=16, n_kv_heads=1, q_len=3,
+                    budget_chunks=1, n_planted=0),
+    "no_sink_batch2": dict(n_blocks=3, block_size=256, sink_size=0, budget_chunks=2, q_len=7,
+                           batch=2, n_planted=0),
 }
 
 
