@@ -721,9 +721,20 @@ phase2_kernel(P2Args a) {
   constexpr int AHEAD = NSLOT - 1;
   __shared__ __attribute__((aligned(1024))) char smem[NSLOT * Stage<D>::BYTES];
 
+  // Workgroups take the shard parts first and the short self parts last, so
+  // that the long parts all start in the first waves of workgroups and finish
+  // together (interleaved self parts staggered them and left a tail).
   int w = blockIdx.x;
-  const int p = w % a.n_parts;
-  w /= a.n_parts;
+  const int n_big = a.n_shards * a.splits;
+  const int total_big = a.batch * a.hkv * a.n_rg * n_big;
+  int p;
+  if (w < total_big) {
+    p = w % n_big;
+    w /= n_big;
+  } else {
+    p = n_big;
+    w -= total_big;
+  }
   const int rg = w % a.n_rg;
   w /= a.n_rg;
   const int g = w % a.hkv;
