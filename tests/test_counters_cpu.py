@@ -47,3 +47,31 @@ def test_template_forms_are_told_apart():
     assert counters.short_name("void pulsar::phase1_kernel<128, false>(pulsar::P1Args)") == "phase1_kernel"
     assert counters.short_name("void pulsar::phase1_kernel<128, true>(pulsar::P1Args)") == "phase1_kernel_prefix_rows"
     assert counters.short_name("void pulsar::phase2_kernel<64, true>(pulsar::P2Args)") == "phase2_kernel_decode"
+
+
+def test_matrix_summary_per_dispatch_and_over_compute(tmp_path):
+    from long_context_blockwise_max_amd import matrix_counters as M
+    import workloads as W
+    p1 = "void pulsar::phase1_kernel<128, false>(pulsar::P1Args)"
+    w = W.CONFIGS["tiny"]
+    alg = M.algorithmic_flops(w, "phase1_kernel")
+    mops = alg * 1.25 / 512.0                # 25 % over-compute, split over 2 instances
+    path = tmp_path / "m.csv"
+    with open(path, "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(HEAD)
+        for disp in (1, 2):
+            for cname, vals in ((M.MOPS, [mops / 2, mops / 2]), (M.BUSY, [300.0, 212.0]),
+                                (M.GUI, [8.0])):
+                for v in vals:
+                    wr.writerow([disp, disp, "Agent 1", 1, 1, 1, 64, 1, p1, 256, 0, 0, 8, 0, 16,
+                                 cname, v, 0, 1])
+    rows = M.per_kernel(str(path))
+    e = rows["phase1_kernel"]
+    assert e["dispatches"] == 2
+    assert abs(e["mfma_flop"] / alg - 1.25) < 1e-9
+    # busy summed over instances; active cycles arrive summed over the 8 XCDs
+    assert abs(e["mfma_busy"] - 512.0 / 1024) < 1e-12
+    md = tmp_path / "m.md"
+    M.main(["--pmc", str(path), "--workload", "tiny", "--summary", str(md)])
+    assert "1.250" in md.read_text()
