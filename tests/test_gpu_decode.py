@@ -6,7 +6,7 @@ import pytest
 
 import workloads as W
 from oracle import attention as OA
-from tests.gpu_cases import LSE_ABS, Case, assert_close, log, torch_cuda
+from tests.gpu_cases import LSE_ABS, Case, assert_close, log, rope_spec, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -33,14 +33,22 @@ CASES = {
     "decode_batch": dict(n_blocks=5, block_size=512, q_len=1, batch=3, n_planted=0),
     "g4_d128": dict(n_blocks=2, block_size=640, n_q_heads=8, n_kv_heads=2, head_dim=128, q_len=5,
                     budget_chunks=2, n_planted=0, batch=2),
+    # Llama-3.1 frequency scaling in the appended keys and the decoded queries
+    "llama3": dict(n_blocks=3, block_size=2048, n_q_heads=8, n_kv_heads=2, head_dim=128, q_len=2,
+                   budget_chunks=2, n_planted=0, rope_scaling=1),
 }
+# generated tokens per case (long_gen: the self cache grows past 8, 16 and 24 tokens,
+# so the zero-padded tail of the value runs moves several times)
+N_GEN = {"long_gen": 22}
+CASES["long_gen"] = dict(n_blocks=2, block_size=256, q_len=3, batch=2, n_planted=0)
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_generation_steps_match_the_oracle(name):
     torch = torch_cuda()
     w = W.with_(W.CONFIGS["tiny"], name=name, **CASES[name])
-    n_gen = 3
+    n_gen = N_GEN.get(name, 3)
+    base = rope_spec(w)
     case = Case(w)
     case.run()
     gq, gk, gv = W.generated(w, n_gen)
@@ -62,7 +70,7 @@ def test_generation_steps_match_the_oracle(name):
             kc, vc = retained[s]
             want_o, want_lse = OA.dense_decode_attention(
                 W.bf16_bits_to_f64(gq[step, s]), kc, vc, W.bf16_bits_to_f64(ks),
-                W.bf16_bits_to_f64(vs), w.context_len, w.rope_base)
+                W.bf16_bits_to_f64(vs), w.context_len, base)
             assert_close(o[s], want_o, f"{name} decode step {step} seq {s} O")
             assert_close(lse[s], want_lse, f"{name} decode step {step} seq {s} LSE",
                          max_abs=LSE_ABS, mean_abs=LSE_ABS)
