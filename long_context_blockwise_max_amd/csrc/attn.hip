@@ -706,6 +706,19 @@ struct P2Args {
   int32_t n_self;       // self tokens; the Lq queries are the last Lq of them
   int32_t vs_ld;        // >= n_self rounded up to 8
   float scale_log2;
+  // Decode form only: when q_raw is set, q is not used and the kernel rotates
+  // the pre-RoPE query rows itself (token t at position q_pos0 + t).
+  const uint16_t* q_raw;
+  int64_t q_pos0;
+  double rope_base;
+  int32_t rope_scaling;
+};
+
+// cos / sin table of the in-kernel query rotation: at most 32 tokens x D/2 pairs
+template <int D>
+struct QTab {
+  static constexpr int MAX_TOK = 32;
+  static constexpr int BYTES = MAX_TOK * (D / 2) * 8;
 };
 
 // KSPLIT: the decode form (all query rows of the workgroup in one 32-row wave),
@@ -719,7 +732,9 @@ phase2_kernel(P2Args a) {
   // otherwise one tile ahead (two slots).
   constexpr int NSLOT = KSPLIT ? 4 : 2;
   constexpr int AHEAD = NSLOT - 1;
-  __shared__ __attribute__((aligned(1024))) char smem[NSLOT * Stage<D>::BYTES];
+  // one LDS object: the slots, then (decode form) the query rotation table
+  constexpr int TAB = KSPLIT ? QTab<D>::BYTES : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[NSLOT * Stage<D>::BYTES + TAB];
 
   // Workgroups take the shard parts first and the short self parts last, so
   // that the long parts all start in the first waves of workgroups and finish
@@ -780,14 +795,13 @@ phase2_kernel(P2Args a) {
   bf16x8 qf[NQ][D / 16];
   const bool wave_active = key_split ? wave < NSUB : row_base < n_rows;
   const int fr = row_base + lr;
-  {
-    const uint16_t* qrow = nullptr;
-    if (fr < n_rows) {
-      const int hh = fr / a.lq, t = fr % a.lq;
-      qrow = a.q + (((int64_t)bb * a.lq + t) * a.hq + g * a.group + hh) * D;
-    }
-    load_q<D>(qrow, qf[0]);
+  const bool rotate_q = KSPLIT && a.q_raw != nullptr;
+  const uint16_t* qrow = nullptr;
+  if (fr < n_rows) {
+    const int hh = fr / a.lq, t = fr % a.lq;
+    qrow = (rotate_q ? a.q_raw : a.q) + (((int64_t)bb * a.lq + t) * a.hq + g * a.group + hh) * D;
   }
+  load_q<D>(qrow, qf[0]);   // pre-RoPE when rotate_q: turned once the table is ready
   const int tok = fr % a.lq;
 
   FlashState<D, NQ> st;
@@ -813,8 +827,37 @@ phase2_kernel(P2Args a) {
   // loads of the AHEAD - 1 newest tiles may still be in flight.
   constexpr int ND = KTile<D>::NI + VTile<D>::NI;
   auto slot = [&](int t) __attribute__((always_inline)) { return smem + (t % NSLOT) * Stage<D>::BYTES; };
+  // Decode form with a pre-RoPE query: cos / sin of every (token, pair) into the
+  // table before the first tiles are staged (an LDS store issued while the tile
+  // loads are in flight would first wait for all of them).
+  float2* tab = reinterpret_cast<float2*>(smem + NSLOT * Stage<D>::BYTES);
+  if (rotate_q) {
+    for (int e = threadIdx.x; e < a.lq * (D / 2); e += NTHR) {
+      float c, sn;
+      rope_cos_sin(a.q_pos0 + e / (D / 2), e % (D / 2), D / 2, a.rope_base, a.rope_scaling, &c, &sn);
+      tab[e] = make_float2(c, sn);
+    }
+  }
 #pragma unroll
   for (int u = 0; u < AHEAD; ++u) stage_tile<D>(slot(u), kbase, vbase, v_ld, src_of(u));
+  if (rotate_q) {
+    // Each lane turns the pairs (i, i + D/2) it holds: i = 16 ks + 8 half + j for
+    // ks < D/32, the partner in fragment ks + D/32.
+    tile_barrier_n<AHEAD * ND>();   // the table is written; the tiles may still be in flight
+    if (qrow) {
+      const int half = (threadIdx.x & 63) >> 5;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float2 cs = tab[tok * (D / 2) + 16 * ks + 8 * half + j];
+          float y1, y2;
+          rope_pair((float)qf[0][ks][j], (float)qf[0][ks + D / 32][j], cs.x, cs.y, y1, y2);
+          qf[0][ks][j] = (__bf16)y1;
+          qf[0][ks + D / 32][j] = (__bf16)y2;
+        }
+    }
+  }
   const float sl2 = a.scale_log2;
   for (int t = 0; t < n_tiles; ++t) {
     tile_barrier_n<(AHEAD - 1) * ND>();   // tile t has landed; every wave is past its reads of tile t-1
@@ -906,11 +949,19 @@ Phase2Geometry phase2_geometry(int32_t batch, int32_t n_shards, int32_t shard_le
   return g;
 }
 
+bool phase2_decode_form(const Phase2Geometry& g) {
+  return g.n_row_groups == 1 && (g.n_q_heads / g.n_kv_heads) * g.q_len <= 32;
+}
+
 int launch_phase2(const Phase2Geometry& g, const uint16_t* q_rot, const uint16_t* k_cache,
                   const uint16_t* v_cache, const SelfShard& self, float* o_part,
-                  float* lse_part, hipStream_t stream) {
+                  float* lse_part, hipStream_t stream, const RawQuery* raw) {
   P2Args a;
   a.q = q_rot;
+  a.q_raw = raw ? raw->q : nullptr;
+  a.q_pos0 = raw ? raw->pos0 : 0;
+  a.rope_base = raw ? raw->base : 0.0;
+  a.rope_scaling = raw ? raw->scaling : 0;
   a.kc = k_cache;
   a.vc = v_cache;
   a.ks = self.k;
@@ -933,7 +984,8 @@ int launch_phase2(const Phase2Geometry& g, const uint16_t* q_rot, const uint16_t
   a.n_rg = g.n_row_groups;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.head_dim));
   const int64_t grid = (int64_t)g.batch * g.n_kv_heads * g.n_row_groups * g.n_parts;
-  const bool ksplit = g.n_row_groups == 1 && (g.n_q_heads / g.n_kv_heads) * g.q_len <= 32;
+  const bool ksplit = phase2_decode_form(g);
+  if (raw && (!ksplit || g.q_len > QTab<128>::MAX_TOK)) return -1;
   if (g.head_dim == 128) {
     if (ksplit) hipLaunchKernelGGL((phase2_kernel<128, true>), dim3(grid), dim3(NTHR), 0, stream, a);
     else hipLaunchKernelGGL((phase2_kernel<128, false>), dim3(grid), dim3(NTHR), 0, stream, a);

@@ -388,11 +388,16 @@ int pulsar_phase2_decode(const pulsar_attn* a, int32_t batch, int32_t n_shards,
   uint16_t* q_rot = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + l.q_rot);
   hipStream_t s = as_stream(stream);
   // query token t is self token n_self - q_len + t
-  if (launch_phase2_prep(qq, nullptr, nullptr, batch, q_len, a->n_q_heads, a->n_kv_heads,
-                         a->head_dim, self_pos0 + n_self - q_len, a->rope_base, a->rope_scaling, 8, q_rot,
-                         nullptr,
+  const int64_t q_pos0 = self_pos0 + n_self - q_len;
+  // The decode form rotates the query rows inside the attention launch; other
+  // shapes rotate them into the workspace first.
+  const bool rotate_inside = phase2_decode_form(pg);
+  if (!rotate_inside &&
+      launch_phase2_prep(qq, nullptr, nullptr, batch, q_len, a->n_q_heads, a->n_kv_heads,
+                         a->head_dim, q_pos0, a->rope_base, a->rope_scaling, 8, q_rot, nullptr,
                          nullptr, s))
     return PULSAR_EHIP;
+  const RawQuery raw{qq, q_pos0, a->rope_base, a->rope_scaling};
   SelfShard self{};
   self.k = k_self_cache;
   self.v = v_self_cache;
@@ -400,8 +405,10 @@ int pulsar_phase2_decode(const pulsar_attn* a, int32_t batch, int32_t n_shards,
   self.v_seq = (int64_t)a->n_kv_heads * a->head_dim * cap;
   self.n = n_self;
   self.v_ld = cap;
-  return launch_phase2(pg, q_rot, k_cache, v_cache, self, o_part, lse_part, s) == 0 ? PULSAR_OK
-                                                                                       : PULSAR_EHIP;
+  return launch_phase2(pg, q_rot, k_cache, v_cache, self, o_part, lse_part, s,
+                       rotate_inside ? &raw : nullptr) == 0
+             ? PULSAR_OK
+             : PULSAR_EHIP;
 }
 
 int pulsar_lse_merge(int32_t batch, int32_t n_parts, int32_t q_len, int32_t n_q_heads,

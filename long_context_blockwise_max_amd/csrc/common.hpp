@@ -57,6 +57,14 @@ __device__ __forceinline__ void rope_cos_sin(int64_t pos, int i, int half, doubl
   *s = (float)sd;
 }
 
+// The pair (a, b) turned by the angle with cosine c and sine s, one fused
+// multiply-add per output.  Every rotation of a query or key goes through this
+// function, so all of them round identically.
+__device__ __forceinline__ void rope_pair(float a, float b, float c, float s, float& y1, float& y2) {
+  y1 = fmaf(a, c, -(b * s));
+  y2 = fmaf(b, c, a * s);
+}
+
 // The value of a lane in the other half of the wave (lane ^ 32), via
 // v_permlane32_swap: lanes 0-31 receive it in the second result, lanes 32-63
 // in the first.

@@ -74,10 +74,23 @@ struct SelfShard {
   int32_t n, v_ld;
 };
 
-// q_rot [B][Lq][Hq][d] already rotated
+// Pre-RoPE query rows for the kernel to rotate itself (token t at pos0 + t).
+struct RawQuery {
+  const uint16_t* q;
+  int64_t pos0;
+  double base;
+  int32_t scaling;
+};
+
+// true when the launch takes the decode form: every query row of a KV head fits
+// one 32-row wave (at most 32 query tokens)
+bool phase2_decode_form(const Phase2Geometry& g);
+
+// q_rot [B][Lq][Hq][d] already rotated; or raw != nullptr (decode form only):
+// the kernel rotates raw->q [B][Lq][Hq][d] itself and q_rot is not read
 int launch_phase2(const Phase2Geometry& g, const uint16_t* q_rot, const uint16_t* k_cache,
                   const uint16_t* v_cache, const SelfShard& self, float* o_part,
-                  float* lse_part, hipStream_t stream);
+                  float* lse_part, hipStream_t stream, const RawQuery* raw = nullptr);
 
 // Append n_new tokens to self caches of capacity cap holding n_self tokens:
 // k_new / v_new [B][n_new][Hkv][d] pre-RoPE, token j at position pos0 + n_self + j;

@@ -42,9 +42,11 @@ __device__ __forceinline__ void rotate_chunk(const uint16_t* src, uint16_t* dst,
   for (int e = 0; e < 4; ++e) {
     const float a0 = bf16_to_f32(x1[e] & 0xffffu), a1 = bf16_to_f32(x1[e] >> 16);
     const float b0 = bf16_to_f32(x2[e] & 0xffffu), b1 = bf16_to_f32(x2[e] >> 16);
-    const float c0 = cs[2 * e], c1 = cs[2 * e + 1], s0 = sn[2 * e], s1 = sn[2 * e + 1];
-    y1[e] = pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
-    y2[e] = pack_bf16x2(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+    float u0, v0, u1, v1;
+    rope_pair(a0, b0, cs[2 * e], sn[2 * e], u0, v0);
+    rope_pair(a1, b1, cs[2 * e + 1], sn[2 * e + 1], u1, v1);
+    y1[e] = pack_bf16x2(u0, u1);
+    y2[e] = pack_bf16x2(v0, v1);
   }
   *(u32x4*)(dst + 8 * c) = y1;
   *(u32x4*)(dst + HALF + 8 * c) = y2;
