@@ -75,3 +75,21 @@ def test_matrix_summary_per_dispatch_and_over_compute(tmp_path):
     md = tmp_path / "m.md"
     M.main(["--pmc", str(path), "--workload", "tiny", "--summary", str(md)])
     assert "1.250" in md.read_text()
+
+
+def test_trace_summary_reads_the_top_kernels_view(tmp_path):
+    import sqlite3
+    from long_context_blockwise_max_amd import trace_summary as T
+    db = tmp_path / "r.db"
+    con = sqlite3.connect(db)
+    con.execute("create table top_kernels (name text, total_calls int, total_duration real, "
+                "average real, percentage real)")
+    con.execute("insert into top_kernels values ('void pulsar::phase1_kernel<128, false>(pulsar::P1Args)',"
+                " 6, 189528.9, 31588.15, 93.78)")
+    con.commit()
+    con.close()
+    rows = T.top_kernels(str(db))
+    assert rows == [("void pulsar::phase1_kernel<128, false>(pulsar::P1Args)", 6, 189528.9, 31588.15, 93.78)]
+    md = tmp_path / "t.md"
+    T.main(["--db", str(db), "--title", "Kernel trace", "--summary", str(md), "--command", "rocprofv3 ..."])
+    assert "| `void pulsar::phase1_kernel<128, false>` | 6 | 189528.9 | 31588.2 | 93.78 |" in md.read_text()
