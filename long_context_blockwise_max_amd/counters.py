@@ -41,6 +41,10 @@ def short_name(full: str) -> str:
             return k
     if COPY_MARK in full:
         return "copy"
+    if "reduce_kernel" in full and "sum_functor" in full:
+        return "cache_evict_read"       # the read pass that evicts the cache before Phase 2
+    if "FillFunctor" in full:
+        return "fill"
     return full.split("(")[0][-60:]
 
 
