@@ -44,15 +44,25 @@ def parse():
 KERNEL_SOURCES = ("attn.hip", "common.hpp")
 
 
+def code_text(src: str) -> str:
+    """C++ source without comments and with whitespace collapsed: what the
+    compiler sees (string literals in these sources hold no comment markers)."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash():
-    """Hash of the attention kernels' sources: counter readings taken on other
-    sources no longer describe the kernel and are not reported."""
+    """Hash of the attention kernels' code (comments and layout ignored): counter
+    readings taken on other code no longer describe the kernel and are not
+    reported."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "long_context_blockwise_max_amd", "csrc")
     for f in KERNEL_SOURCES:
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(d, f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -12,7 +12,7 @@ KiB to bytes that really crossed the memory interface, applied to every kernel.
         --copy-mib 1024 --workload 128k --out profiles/hbm_traffic.json \\
         --summary profiles/hbm_traffic_128k.md --command "<the rocprofv3 lines>"
 
-The JSON keeps the hash of the attention kernels' sources the counters were
+The JSON keeps the hash of the attention kernels' code (comments ignored) the counters were
 taken on; bench.py reports the traffic only while that hash still matches.
 """
 from __future__ import annotations
@@ -153,7 +153,7 @@ def main(argv=None):
              f"Calibration: one elementwise copy of {a.copy_mib} MiB read "
              f"{fetch['copy'][0]:.0f} KiB (FETCH_SIZE) and wrote {write['copy'][0]:.0f} KiB "
              f"(WRITE_SIZE): scale factors {f_scale:.4f} (fetch), {w_scale:.4f} (write).", "",
-             f"Kernel sources hash: {src}", "",
+             f"Kernel code hash (comments ignored): {src}", "",
              "| kernel | dispatches | fetch GB | write GB | total GB | algorithmic GB | ratio |",
              "|---|---:|---:|---:|---:|---:|---:|"]
     for k, e in sorted(rows.items(), key=lambda kv: -kv[1]["bytes_per_launch"]):

@@ -19,12 +19,15 @@
 // and row sum need one exchange with lane l ^ 32 (v_permlane32_swap); the
 // rescale of O touches only the lane's own registers.
 //
-// Tiles are staged with direct global->LDS loads (global_load_lds_dwordx4), two
-// stages deep, one barrier per tile; the 16-byte chunks of every LDS row are
-// XOR-swizzled so that fragment reads are bank-conflict free.
+// Tiles are staged with direct global->LDS loads (global_load_lds_dwordx4), one
+// barrier per tile: two slots, one tile ahead, for Phase 1 and the Phase-2
+// query; four slots, three tiles ahead, for the Phase-2 decode form, which
+// streams from HBM with little work per tile.  The 16-byte chunks of every LDS
+// row are XOR-swizzled so that fragment reads are bank-conflict free.
 //
-// Softmax runs in base 2: t = (q.k) * log2(e) / sqrt(d), p = exp2(t - m).  P is
-// rounded to bf16 for the PV MFMA; the running sum uses the fp32 p.
+// Softmax runs in base 2: t = (q.k) * log2(e) / sqrt(d), p = exp2(t - m), with
+// the reference maximum m raised lazily (see kRescaleSlack).  P is rounded to
+// bf16 for the PV MFMA; the running sum uses the fp32 p.
 #include <math.h>
 
 #include <algorithm>

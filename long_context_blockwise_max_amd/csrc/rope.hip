@@ -15,6 +15,11 @@
 //   phase2_prep  Phase-2 prep in one launch: rotated query rows and rotated
 //                self keys (positions pos0 + t), and the d-major copy of the
 //                self values
+//   self_append  generation: a new token's rotated keys into the self key
+//                cache and its values into the d-major self value cache
+//
+// (The Phase-2 decode form rotates its query rows inside the attention launch,
+// with the same angle and rotation functions.)
 //
 // In rope_fill one thread per (token, 8-wide pair chunk c) derives cos/sin for
 // the 8 frequencies 8c .. 8c+7 once and applies them to elements [8c, 8c+8) and

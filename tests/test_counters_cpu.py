@@ -93,3 +93,12 @@ def test_trace_summary_reads_the_top_kernels_view(tmp_path):
     md = tmp_path / "t.md"
     T.main(["--db", str(db), "--title", "Kernel trace", "--summary", str(md), "--command", "rocprofv3 ..."])
     assert "| `void pulsar::phase1_kernel<128, false>` | 6 | 189528.9 | 31588.2 | 93.78 |" in md.read_text()
+
+
+def test_code_hash_ignores_comments_and_layout():
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* plain */ }\n"
+    b = "int f(int x) {\n  // twice x\n  return 2 * x;\n}\n"
+    c = "int f(int x) { return 3 * x; }"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
+    assert "s_waitcnt vmcnt(0)" in bench.code_text('asm volatile("s_waitcnt vmcnt(0)");  // wait')
