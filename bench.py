@@ -216,7 +216,7 @@ def main():
     from long_context_blockwise_max_amd import costs as C
     from long_context_blockwise_max_amd.pipeline import Geometry, HotPath
 
-    w = W.CONFIGS[args.config]
+    w = W.WORKLOADS[args.config]
     geo = Geometry(w.n_blocks, w.block_size, w.chunk_size, w.budget_chunks, w.sink_size,
                    w.vocab_size, w.n_q_heads, w.n_kv_heads, w.head_dim, w.q_len, w.batch,
                    w.rope_base, True)

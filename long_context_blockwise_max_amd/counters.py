@@ -115,7 +115,7 @@ def main(argv=None):
     copy_bytes = float(a.copy_mib) * (1 << 20)
     f_scale = copy_bytes / (fetch["copy"][0] * 1024.0)
     w_scale = copy_bytes / (write["copy"][0] * 1024.0)
-    w = W.CONFIGS[a.workload]
+    w = W.WORKLOADS[a.workload]
 
     rows = {}
     for k in sorted(set(fetch) & set(write)):

@@ -125,7 +125,7 @@ def main(argv=None):
     sys.path.insert(0, root)
     import workloads as W
 
-    w = W.CONFIGS[a.workload]
+    w = W.WORKLOADS[a.workload]
     rows = per_kernel(a.pmc)
     lines = [f"# Matrix-core work per launch, {a.workload} workload", "",
              "Command:", "", "```", a.command.strip(), "```", "",

@@ -53,7 +53,7 @@ def test_matrix_summary_per_dispatch_and_over_compute(tmp_path):
     from long_context_blockwise_max_amd import matrix_counters as M
     import workloads as W
     p1 = "void pulsar::phase1_kernel<128, false>(pulsar::P1Args)"
-    w = W.CONFIGS["tiny"]
+    w = W.WORKLOADS["tiny"]
     alg = M.algorithmic_flops(w, "phase1_kernel")
     mops = alg * 1.25 / 512.0                # 25 % over-compute, split over 2 instances
     path = tmp_path / "m.csv"

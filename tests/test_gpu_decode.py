@@ -46,7 +46,7 @@ CASES["long_gen"] = dict(n_blocks=2, block_size=256, q_len=3, batch=2, n_planted
 @pytest.mark.parametrize("name", list(CASES))
 def test_generation_steps_match_the_oracle(name):
     torch = torch_cuda()
-    w = W.with_(W.CONFIGS["tiny"], name=name, **CASES[name])
+    w = W.with_(W.WORKLOADS["tiny"], name=name, **CASES[name])
     n_gen = N_GEN.get(name, 3)
     base = rope_spec(w)
     case = Case(w)
@@ -81,7 +81,7 @@ def test_decode_of_the_query_tokens_is_the_query_phase():
     those tokens is the query phase with its self shard."""
     torch = torch_cuda()
     from long_context_blockwise_max_amd import binding as B
-    w = W.with_(W.CONFIGS["tiny"], name="consistency", **CASES["g4_d128"])
+    w = W.with_(W.WORKLOADS["tiny"], name="consistency", **CASES["g4_d128"])
     case = Case(w)
     case.run()
     path = case.path

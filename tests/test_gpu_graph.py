@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 
 def test_generation_graph_replays_match_eager_steps():
     torch = torch_cuda()
-    w = W.with_(W.CONFIGS["tiny"], name="graph", n_blocks=5, block_size=512, q_len=2, batch=2,
+    w = W.with_(W.WORKLOADS["tiny"], name="graph", n_blocks=5, block_size=512, q_len=2, batch=2,
                 n_planted=0)
     n = 4
     case = Case(w)

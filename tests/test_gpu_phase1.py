@@ -93,7 +93,7 @@ SMALL = {
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_phase1_small_all_rows(name):
-    w = W.with_(W.CONFIGS["tiny"], name=name, **SMALL[name])
+    w = W.with_(W.WORKLOADS["tiny"], name=name, **SMALL[name])
     case = Case(w)
     case.run()
     _cache_check(case)
@@ -102,7 +102,7 @@ def test_phase1_small_all_rows(name):
 
 def test_phase1_is_deterministic():
     torch = torch_cuda()
-    case = Case(W.CONFIGS["tiny"])
+    case = Case(W.WORKLOADS["tiny"])
     case.run()
     a = case.path.o.clone()
     case.run()
@@ -111,7 +111,7 @@ def test_phase1_is_deterministic():
 
 @pytest.mark.parametrize("name", ["32k", "128k", "128k_star", "512k"])
 def test_phase1_full_size_sampled(name):
-    w = W.CONFIGS[name]
+    w = W.WORKLOADS[name]
     case = Case(w, extra_seqs=False)
     case.run()
     rows = sample_rows(w, per_block_random=1 if w.n_blocks > 8 else 3, seed=w.seed,
@@ -122,7 +122,7 @@ def test_phase1_full_size_sampled(name):
 def test_prepare_then_attend_equals_encode():
     """The two halves of the Phase-1 call, issued apart, give encode's results bit for bit."""
     torch = torch_cuda()
-    w = W.with_(W.CONFIGS["tiny"], name="split", **SMALL["ragged_g2_d64"])
+    w = W.with_(W.WORKLOADS["tiny"], name="split", **SMALL["ragged_g2_d64"])
     case = Case(w)
     case.run()
     o, kc, vc = case.path.o.clone(), case.path.k_cache.clone(), case.path.v_cache.clone()

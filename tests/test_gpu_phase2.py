@@ -65,7 +65,7 @@ SMALL = {
 @pytest.mark.parametrize("with_self", [True, False])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_phase2_small(name, with_self):
-    w = W.with_(W.CONFIGS["tiny"], name=name, **SMALL[name])
+    w = W.with_(W.WORKLOADS["tiny"], name=name, **SMALL[name])
     case = Case(w, with_self=with_self)
     case.run()
     _compare(case, range(w.batch))
@@ -73,14 +73,14 @@ def test_phase2_small(name, with_self):
 
 @pytest.mark.parametrize("name", ["32k", "128k"])
 def test_phase2_full_size(name):
-    w = W.CONFIGS[name]
+    w = W.WORKLOADS[name]
     case = Case(w)
     case.run()
     _compare(case, [0])
 
 
 def test_phase2_full_size_decode_batch():
-    w = W.CONFIGS["512k"]
+    w = W.WORKLOADS["512k"]
     case = Case(w)
     case.run()
     _compare(case, [0, 1, w.batch - 1])

@@ -30,7 +30,7 @@ def _prefix_last(case):
 @pytest.mark.parametrize("name", [n for n in SMALL if SMALL[n].get("n_blocks", 4) > 1] + ["single_block"])
 def test_prefix_rows_small_all_rows(name):
     torch_cuda()
-    w = W.with_(W.CONFIGS["tiny"], name=name, **SMALL[name])
+    w = W.with_(W.WORKLOADS["tiny"], name=name, **SMALL[name])
     case = Case(w)
     n = _run(case)
     pre = _prefix_last(case)
@@ -46,7 +46,7 @@ def test_prefix_rows_small_all_rows(name):
 @pytest.mark.parametrize("name", ["128k", "32k"])
 def test_prefix_rows_full_size_sampled(name):
     torch_cuda()
-    w = W.CONFIGS[name]
+    w = W.WORKLOADS[name]
     case = Case(w, extra_seqs=False)
     n = _run(case)
     pre = _prefix_last(case)

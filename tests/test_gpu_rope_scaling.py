@@ -16,7 +16,7 @@ def test_llama3_scaled_rope_matches_the_oracle(d):
     import torch
     torch_cuda()
     # positions up to ~40K, so frequencies in all three regimes turn by many periods
-    w = W.with_(W.CONFIGS["tiny"], name=f"llama3_d{d}", n_blocks=5, block_size=8192 if d == 64 else 4096,
+    w = W.with_(W.WORKLOADS["tiny"], name=f"llama3_d{d}", n_blocks=5, block_size=8192 if d == 64 else 4096,
                 n_q_heads=8, n_kv_heads=2, head_dim=d, budget_chunks=2, n_planted=0, q_len=3,
                 rope_scaling=1)
     base = rope_spec(w)

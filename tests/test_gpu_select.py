@@ -42,7 +42,7 @@ def check(tok, n_blocks, block_size, chunk, k, vocab):
 
 @pytest.mark.parametrize("name", ["tiny", "32k", "128k", "128k_star", "512k"])
 def test_select_workloads(name):
-    w = W.CONFIGS[name]
+    w = W.WORKLOADS[name]
     check(W.tokens(w), w.n_blocks, w.block_size, w.chunk_size, w.budget_chunks, w.vocab_size)
 
 
@@ -102,7 +102,7 @@ def test_select_flags_out_of_range_ids():
 
 
 def test_select_is_deterministic():
-    w = W.CONFIGS["128k"]
+    w = W.WORKLOADS["128k"]
     tok = W.tokens(w)
     a = run_select(tok, w.n_blocks, w.block_size, w.chunk_size, w.budget_chunks, w.vocab_size)
     b = run_select(tok, w.n_blocks, w.block_size, w.chunk_size, w.budget_chunks, w.vocab_size)

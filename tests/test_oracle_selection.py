@@ -90,7 +90,7 @@ def test_df_counts_blocks_by_brute_force():
 
 @pytest.mark.parametrize("name", ["tiny"])
 def test_summary_length_equals_budget_and_order(name):
-    w = W.CONFIGS[name]
+    w = W.WORKLOADS[name]
     t = W.tokens(w)
     sel, df, score = S.select(t, w.n_blocks, w.block_size, w.chunk_size, w.budget_chunks, w.vocab_size)
     assert sel.shape == (w.n_blocks, w.budget_chunks)
@@ -168,7 +168,7 @@ def test_sink_overlap_is_not_deduplicated():
 
 
 def test_zipf_stream_is_reproducible_and_bounded():
-    w = W.CONFIGS["tiny"]
+    w = W.WORKLOADS["tiny"]
     t1, t2 = W.tokens(w), W.tokens(w)
     np.testing.assert_array_equal(t1, t2)
     assert t1.min() >= 0 and t1.max() < w.vocab_size

@@ -73,7 +73,7 @@ def budget_chunks_for(block_size: int, chunk_size: int = 32, frac: float = 0.125
     return int(block_size * frac) // chunk_size
 
 
-CONFIGS = {
+WORKLOADS = {
     "tiny": Workload("tiny", 1, 4, 1024, 64, 32, 4, 32000, 16, 4, 2, 64, 32, 1),
     "32k": Workload("32k", 2, 4, 8192, 64, 32, 32, 128256, 0, 32, 8, 128, 64, 1),
     "128k": Workload("128k", 3, 8, 16384, 64, 32, 64, 128256, 0, 32, 8, 128, 64, 1),
