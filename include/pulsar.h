@@ -5,6 +5,7 @@
  * Anchor: Statistical Context Summarization for Distributed Systems via Pulsar
  * Attention":
  *   pulsar_select         Section 2.1: Max-IDF summary selection from token IDs
+ *                         (pulsar_select_method: the ablation's other scores)
  *   pulsar_phase1_encode  Section 2 / 2.1: each block attends over
  *                         [sink || summaries of earlier blocks || own block] at
  *                         original positions and keeps only its own KV
@@ -107,6 +108,41 @@ int32_t pulsar_kept_chunks(const pulsar_geom* g);
 int pulsar_select(const pulsar_geom* g, const int32_t* tok, int32_t* sel,
                   int32_t* chunk_min_df, int32_t* df, void* ws, size_t ws_bytes,
                   void* stream);
+
+/* Summary selection by another chunk score: the alternatives the Dutch technical
+ * summary's ablation compares Max-IDF against ("Dropping the Anchor ..." Section
+ * 2.1 contrasts the maximum with the mean).  The output feeds Phase 1 exactly as
+ * pulsar_select's does.
+ *   PULSAR_SELECT_MAX_IDF   the method's score, as pulsar_select
+ *   PULSAR_SELECT_MEAN_IDF  mean over the chunk's tokens of ln(N / df(t)); an id
+ *                           outside the vocabulary counts as idf 0 (df = N).
+ *                           TF-IDF with term counts within the chunk ranks the same
+ *   PULSAR_SELECT_ENTROPY   Shannon entropy of the chunk's token histogram
+ *                           (more diverse chunks first)
+ *   PULSAR_SELECT_UNIFORM   k chunks per block uniformly at random: chunk c of
+ *                           block j is keyed by the SplitMix64 output with counter
+ *                           j * n_chunks + c + 1 from `seed` (Steele, Lea and
+ *                           Flood, 2014); the k smallest keys are kept
+ *   PULSAR_SELECT_EVEN      chunks floor(m * n_chunks / k), m = 0 .. k-1
+ * Higher scores win; equal scores go to the earlier chunk, decided exactly (mean
+ * IDF and entropy are ranked by integer products over the chunk's positions).
+ * Kept chunks are returned in ascending order, k = pulsar_kept_chunks(g).
+ *   tok   [L] int32 token ids (not read by UNIFORM and EVEN)
+ *   sel   [N][kept] int32 out
+ *   seed  UNIFORM only
+ *   ws    at least pulsar_workspace_bytes(g, NULL) bytes; its first word is the
+ *         status word, set to 1 when a token id lies outside [0, vocab_size)
+ *         (MAX_IDF, MEAN_IDF and ENTROPY read the ids)
+ * Errors: PULSAR_EINVAL (also an unknown method), PULSAR_EWORKSPACE,
+ * PULSAR_EUNSUPPORTED (mean IDF with N^chunk >= 2^256, entropy with
+ * chunk^chunk >= 2^256, or more than 4096 chunks per block), PULSAR_EHIP. */
+#define PULSAR_SELECT_MAX_IDF 0
+#define PULSAR_SELECT_MEAN_IDF 1
+#define PULSAR_SELECT_ENTROPY 2
+#define PULSAR_SELECT_UNIFORM 3
+#define PULSAR_SELECT_EVEN 4
+int pulsar_select_method(const pulsar_geom* g, int32_t method, uint64_t seed, const int32_t* tok,
+                         int32_t* sel, void* ws, size_t ws_bytes, void* stream);
 
 /* Phase-1 context encoding ("Dropping the Anchor ..." Section 2 and 2.1).
  * Block i > 0 attends over [first S tokens || kept chunks of blocks 0..i-1 in

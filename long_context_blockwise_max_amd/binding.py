@@ -21,7 +21,8 @@ PULSAR_EHIP = -3
 PULSAR_EUNSUPPORTED = -4
 
 EXPORTED = (
-    "pulsar_workspace_bytes", "pulsar_kept_chunks", "pulsar_select", "pulsar_phase1_encode",
+    "pulsar_workspace_bytes", "pulsar_kept_chunks", "pulsar_select", "pulsar_select_method",
+    "pulsar_phase1_encode",
     "pulsar_phase1_prepare", "pulsar_phase1_attend", "pulsar_self_append", "pulsar_phase2_decode",
     "pulsar_prefix_rows_len", "pulsar_phase1_prefix_rows",
     "pulsar_phase2_num_parts", "pulsar_phase2_workspace_bytes", "pulsar_phase2_query",
@@ -64,6 +65,8 @@ def lib():
         L.pulsar_kept_chunks.argtypes = [G]
         L.pulsar_kept_chunks.restype = i32
         L.pulsar_select.argtypes = [G, vp, vp, vp, vp, vp, sz, vp]
+        L.pulsar_select_method.argtypes = [G, i32, ctypes.c_uint64, vp, vp, vp, sz, vp]
+        L.pulsar_select_method.restype = ctypes.c_int
         L.pulsar_select.restype = ctypes.c_int
         L.pulsar_phase1_encode.argtypes = [G, A, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pulsar_phase1_encode.restype = ctypes.c_int
@@ -170,6 +173,23 @@ def pulsar_select(geom: Geom, tok, sel, chunk_min_df, df, ws, stream=None):
         _ptr(df, torch.int32, geom.vocab_size, "df", allow_none=True),
         _ptr(ws, torch.uint8, 0, "ws"), ws.numel(), _stream(stream))
     _check(rc, "pulsar_select")
+
+
+SELECT_METHODS = {"max_idf": 0, "mean_idf": 1, "entropy": 2, "uniform": 3, "even": 4}
+
+
+def pulsar_select_method(geom: Geom, method, seed, tok, sel, ws, stream=None):
+    """method: a name of SELECT_METHODS or its number."""
+    import torch
+    m = SELECT_METHODS[method] if isinstance(method, str) else int(method)
+    L = geom.n_blocks * geom.block_size
+    kept = pulsar_kept_chunks(geom)
+    rc = lib().pulsar_select_method(
+        ctypes.byref(geom), m, ctypes.c_uint64(int(seed) & ((1 << 64) - 1)),
+        _ptr(tok, torch.int32, L, "tok", allow_none=m in (3, 4)),
+        _ptr(sel, torch.int32, geom.n_blocks * max(kept, 0), "sel", allow_none=kept <= 0),
+        _ptr(ws, torch.uint8, 0, "ws"), ws.numel(), _stream(stream))
+    _check(rc, "pulsar_select_method")
 
 
 def pulsar_phase1_encode(geom: Geom, attn: Attn, q, k, v, sel, o, k_cache, v_cache, ws,

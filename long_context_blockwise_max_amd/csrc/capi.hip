@@ -161,6 +161,35 @@ int pulsar_select(const pulsar_geom* g, const int32_t* tok, int32_t* sel, int32_
              : PULSAR_EHIP;
 }
 
+int pulsar_select_method(const pulsar_geom* g, int32_t method, uint64_t seed, const int32_t* tok,
+                         int32_t* sel, void* ws, size_t ws_bytes, void* stream) {
+  if (method == PULSAR_SELECT_MAX_IDF) return pulsar_select(g, tok, sel, nullptr, nullptr, ws, ws_bytes, stream);
+  int rc = check_geom(g);
+  if (rc) return rc;
+  if (method < PULSAR_SELECT_MEAN_IDF || method > PULSAR_SELECT_EVEN) return PULSAR_EINVAL;
+  const int32_t kept = kept_chunks(g);
+  const bool reads_tokens = method == PULSAR_SELECT_MEAN_IDF || method == PULSAR_SELECT_ENTROPY;
+  if (reads_tokens && !aligned16(tok)) return PULSAR_EINVAL;
+  if (kept > 0 && !aligned16(sel)) return PULSAR_EINVAL;
+  const int64_t n_chunks = g->block_size / g->chunk_size;
+  if (method != PULSAR_SELECT_EVEN && n_chunks > 4096) return PULSAR_EUNSUPPORTED;  // LDS keys
+  // the exact order keys are products over a chunk's positions held in 256 bits
+  if (method == PULSAR_SELECT_MEAN_IDF && g->chunk_size * log2((double)g->n_blocks) >= 255.5)
+    return PULSAR_EUNSUPPORTED;
+  if (method == PULSAR_SELECT_ENTROPY && g->chunk_size * log2((double)g->chunk_size) >= 255.5)
+    return PULSAR_EUNSUPPORTED;
+  const Layout l = layout(g, nullptr);
+  if (!ws || ws_bytes < l.total) return PULSAR_EWORKSPACE;
+  if (!aligned16(ws)) return PULSAR_EINVAL;
+  char* w = static_cast<char*>(ws);
+  int32_t* status = reinterpret_cast<int32_t*>(w + l.status);
+  int32_t* dfp = reinterpret_cast<int32_t*>(w + l.df);
+  return launch_select_method(method, seed, tok, g->n_blocks, g->block_size, g->chunk_size, kept,
+                              g->vocab_size, sel, dfp, status, as_stream(stream)) == 0
+             ? PULSAR_OK
+             : PULSAR_EHIP;
+}
+
 }  // extern "C"
 
 namespace {

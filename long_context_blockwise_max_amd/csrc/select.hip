@@ -156,4 +156,161 @@ int launch_select(const int32_t* tok, int32_t n_blocks, int32_t block_size, int3
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
+// ------------------------------------------------------- other chunk scores
+// The alternatives the Dutch technical summary's ablation compares against
+// ("Dropping the Anchor ..." Section 2.1 contrasts the maximum with the mean):
+//   mean IDF   mean over the chunk's tokens of ln(N / df) (an id outside the
+//              vocabulary counts as df = N, idf 0)
+//   entropy    Shannon entropy of the chunk's token histogram
+//   uniform    k chunks per block uniformly at random: each chunk's key is the
+//              SplitMix64 output with counter j * n_chunks + c + 1 from the seed
+//              (Steele, Lea and Flood, 2014), the k smallest keys are kept
+//   even       chunks floor(m * n_chunks / k), m = 0 .. k-1
+// Mean IDF is ln N - (1/C) ln prod_pos df(t_pos) and the entropy
+// ln C - (1/C) ln prod_pos c(t_pos), c(t_pos) = count of that token in its
+// chunk, so both fall as an integer product over the chunk's positions rises.
+// Each chunk's product is formed exactly in 256 bits (the launcher checks that
+// it fits), and a chunk is kept when fewer than k chunks of its block have a
+// smaller product, or an equal product and a lower index: the same ties as Max-IDF,
+// decided exactly.  One workgroup per block; the keys sit in LDS and every
+// thread ranks its chunks against all of them.
+
+constexpr int kKeyLimbs = 8;   // 256-bit keys, little-endian 32-bit limbs
+
+__device__ __forceinline__ void key_mul(uint32_t (&k)[kKeyLimbs], uint32_t f) {
+  uint64_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < kKeyLimbs; ++i) {
+    const uint64_t x = (uint64_t)k[i] * f + carry;
+    k[i] = (uint32_t)x;
+    carry = x >> 32;
+  }
+}
+
+__device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + n * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// true when key a (registers) is smaller than key b (LDS)
+__device__ __forceinline__ int key_cmp(const uint32_t (&a)[kKeyLimbs], const uint32_t* b) {
+#pragma unroll
+  for (int i = kKeyLimbs - 1; i >= 0; --i) {
+    const uint32_t y = b[i];
+    if (a[i] != y) return a[i] < y ? -1 : 1;
+  }
+  return 0;
+}
+
+template <int METHOD>   // 1 mean IDF, 2 entropy, 3 uniform
+__global__ void __launch_bounds__(kSelThreads) select_keyed(
+    const int32_t* __restrict__ tok, const int32_t* __restrict__ df, int32_t n_blocks,
+    int32_t block_size, int32_t chunk_size, int32_t kept, int32_t vocab, uint64_t seed,
+    int32_t* __restrict__ sel, int32_t* __restrict__ status) {
+  extern __shared__ uint32_t keys[];   // [n_chunks][kKeyLimbs]
+  __shared__ int wave_tot[kSelWaves];
+  const int n_chunks = block_size / chunk_size;
+  const int j = blockIdx.x;
+  const int32_t* t = tok + (int64_t)j * block_size;
+  bool bad = false;
+  for (int c = threadIdx.x; c < n_chunks; c += blockDim.x) {
+    uint32_t k[kKeyLimbs] = {1u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    if constexpr (METHOD == 3) {
+      const uint64_t z = splitmix64(seed, (uint64_t)j * n_chunks + c + 1);
+      k[0] = (uint32_t)z;
+      k[1] = (uint32_t)(z >> 32);
+    } else {
+      const int32_t* ct = t + c * chunk_size;
+      for (int e = 0; e < chunk_size; ++e) {
+        const int32_t id = ct[e];
+        const bool in_range = id >= 0 && id < vocab;
+        bad |= !in_range;
+        uint32_t f;
+        if constexpr (METHOD == 1) {
+          f = in_range ? (uint32_t)df[id] : (uint32_t)n_blocks;
+        } else {
+          f = 0;
+          for (int e2 = 0; e2 < chunk_size; ++e2) f += ct[e2] == id;
+        }
+        key_mul(k, f);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kKeyLimbs; ++i) keys[c * kKeyLimbs + i] = k[i];
+  }
+  if (bad) atomicOr(status, 1);
+  __syncthreads();
+  int out_base = 0;
+  for (int base = 0; base < n_chunks; base += kSelThreads) {
+    const int c = base + threadIdx.x;
+    bool take = false;
+    if (c < n_chunks) {
+      uint32_t k[kKeyLimbs];
+#pragma unroll
+      for (int i = 0; i < kKeyLimbs; ++i) k[i] = keys[c * kKeyLimbs + i];
+      int better = 0;
+      for (int c2 = 0; c2 < n_chunks && better < kept; ++c2) {
+        const int r = key_cmp(k, keys + c2 * kKeyLimbs);
+        better += (r > 0) || (r == 0 && c2 < c);
+      }
+      take = better < kept;
+    }
+    int out_tot;
+    const int slot = out_base + wg_exclusive_count(take, wave_tot, &out_tot);
+    if (take) sel[(int64_t)j * kept + slot] = c;
+    out_base += out_tot;
+  }
+}
+
+__global__ void __launch_bounds__(256) select_even(int32_t n_blocks, int32_t n_chunks,
+                                                   int32_t kept, int32_t* __restrict__ sel) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)n_blocks * kept) return;
+  const int m = (int)(i % kept);
+  sel[i] = (int32_t)((int64_t)m * n_chunks / kept);
+}
+
+int launch_select_method(int32_t method, uint64_t seed, const int32_t* tok, int32_t n_blocks,
+                         int32_t block_size, int32_t chunk_size, int32_t kept, int32_t vocab,
+                         int32_t* sel, int32_t* df, int32_t* status, hipStream_t stream) {
+  const int n_chunks = block_size / chunk_size;
+  // the status word (and df, for mean IDF) start at zero
+  const int32_t clear_n = method == 1 ? vocab : 0;
+  const int clear_blocks = (int)std::min<int64_t>(1024, ((int64_t)clear_n + 255) / 256 + 1);
+  hipLaunchKernelGGL(select_clear, dim3(clear_blocks), dim3(256), 0, stream, df, clear_n, status);
+  if (kept <= 0) return hipGetLastError() == hipSuccess ? 0 : -3;
+  if (method == 4) {
+    const int64_t n = (int64_t)n_blocks * kept;
+    hipLaunchKernelGGL(select_even, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       n_blocks, n_chunks, kept, sel);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+  }
+  if (method == 1) {
+    const size_t bitmap_bytes = (size_t)((vocab + 31) / 32) * 4;
+    if (bitmap_bytes > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&select_df),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bitmap_bytes) != hipSuccess)
+      return -3;
+    hipLaunchKernelGGL(select_df, dim3(n_blocks), dim3(1024), bitmap_bytes, stream, tok,
+                       block_size, vocab, df, status);
+  }
+  const size_t lds = (size_t)n_chunks * kKeyLimbs * 4;
+  auto go = [&](const void* fn, auto kernel) {
+    if (lds > 65536 &&
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return -3;
+    hipLaunchKernelGGL(kernel, dim3(n_blocks), dim3(kSelThreads), lds, stream, tok, df, n_blocks,
+                       block_size, chunk_size, kept, vocab, seed, sel, status);
+    return 0;
+  };
+  int rc = 0;
+  if (method == 1) rc = go(reinterpret_cast<const void*>(&select_keyed<1>), select_keyed<1>);
+  else if (method == 2) rc = go(reinterpret_cast<const void*>(&select_keyed<2>), select_keyed<2>);
+  else rc = go(reinterpret_cast<const void*>(&select_keyed<3>), select_keyed<3>);
+  if (rc) return rc;
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
 }  // namespace pulsar

@@ -116,6 +116,11 @@ class HotPath:
         B.pulsar_select(self.cgeom, self.tok, self.sel if self.kept > 0 else None,
                         self.chunk_min_df, self.df, self.ws, stream)
 
+    def select_method(self, method, seed=0, stream=None):
+        """Selection by another chunk score (binding.SELECT_METHODS) into sel."""
+        B.pulsar_select_method(self.cgeom, method, seed, self.tok,
+                               self.sel if self.kept > 0 else None, self.ws, stream)
+
     def phase1(self, stream=None):
         B.pulsar_phase1_encode(self.cgeom, self.cattn, self.q, self.k, self.v,
                                self.sel if self.kept > 0 else None, self.o,

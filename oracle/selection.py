@@ -21,12 +21,13 @@ import numpy as np
 
 
 def document_frequency(tokens, n_blocks, block_size, vocab_size):
-    """df[t] = number of blocks j in [0, N) whose tokens include t."""
+    """df[t] = number of blocks j in [0, N) whose tokens include t.  Ids outside
+    [0, vocab_size) name no vocabulary entry and are not counted."""
     tokens = np.asarray(tokens)
     df = np.zeros(vocab_size, dtype=np.int64)
     for j in range(n_blocks):
         present = np.unique(tokens[j * block_size:(j + 1) * block_size])
-        df[present] += 1
+        df[present[(present >= 0) & (present < vocab_size)]] += 1
     return df
 
 

@@ -87,6 +87,26 @@ def test_select_rejects_pointers_and_small_workspace():
 
 
 @needs_lib
+def test_select_method_rejects_bad_arguments():
+    lib = B.lib()
+
+    def sm(g, method, tok=FAKE, sel=FAKE, ws=FAKE, wsb=1 << 30):
+        return lib.pulsar_select_method(ctypes.byref(g), method, 0, tok, sel, ws, wsb, None)
+
+    g = geom()
+    assert sm(g, 5) == B.PULSAR_EINVAL and sm(g, -1) == B.PULSAR_EINVAL   # unknown method
+    assert sm(geom(n_blocks=0), 1) == B.PULSAR_EINVAL
+    assert sm(g, 1, tok=None) == B.PULSAR_EINVAL            # mean IDF reads the tokens
+    assert sm(g, 2, tok=FAKE_MIS) == B.PULSAR_EINVAL        # so does entropy
+    assert sm(g, 1, wsb=16) == B.PULSAR_EWORKSPACE
+    assert sm(g, 4, ws=None) == B.PULSAR_EWORKSPACE
+    # exact order keys must fit 256 bits: N^chunk for mean IDF, chunk^chunk for entropy
+    assert sm(geom(n_blocks=300, block_size=1024, budget_chunks=4), 1) == B.PULSAR_EUNSUPPORTED
+    assert sm(geom(chunk_size=64), 2) == B.PULSAR_EUNSUPPORTED
+    assert sm(geom(block_size=65536, chunk_size=8, budget_chunks=4), 3) == B.PULSAR_EUNSUPPORTED  # > 4096 chunks
+
+
+@needs_lib
 def test_phase1_rejects_bad_arguments():
     lib = B.lib()
     g = geom()

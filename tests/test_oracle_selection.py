@@ -173,3 +173,9 @@ def test_zipf_stream_is_reproducible_and_bounded():
     np.testing.assert_array_equal(t1, t2)
     assert t1.min() >= 0 and t1.max() < w.vocab_size
     assert len(W.planted_positions(w)) == w.n_planted
+
+
+def test_df_skips_ids_outside_the_vocabulary():
+    t = np.array([0, 1, 7, -2, 1, 8, 0, 3], np.int64)       # V = 8: ids 8 and -2 name no entry
+    df = S.document_frequency(t, 2, 4, 8)
+    assert df.tolist() == [2, 2, 0, 1, 0, 0, 0, 1]
