@@ -107,6 +107,31 @@ def prefix_rows(path, w, stream, reps=3):
             "algorithmic_flop": flop}
 
 
+def selection_methods(path, w, stream, reps=5):
+    """Every selection method on the workload's tokens, one launch sequence each
+    (median of reps, events on the launch stream); the Max-IDF selection is
+    restored afterwards so that later work sees the method's own summaries."""
+    import numpy as np
+    import torch
+
+    from long_context_blockwise_max_amd import binding as B
+
+    out = {}
+    for name in B.SELECT_METHODS:
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            path.select_method(name, seed=w.seed)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        out[name] = {"us": round(float(np.median(ms)) * 1e3, 2)}
+    path.select()
+    torch.cuda.synchronize()
+    return out
+
+
 def generation(path, w, n_tokens, stream):
     """Generated tokens after the query: each step appends the token's key and
     value to the query host's self cache, attends its query to every retained
@@ -338,6 +363,7 @@ def main():
                             "traffic": recorded_traffic(w.name, "phase2_kernel")},
     }
     out["prefix_rows"] = prefix_rows(path, w, stream)
+    out["selection_methods"] = selection_methods(path, w, stream)
     if args.gen_tokens > 0:
         out["generation"] = generation(path, w, args.gen_tokens, stream)
     if not args.no_cpu_baseline:

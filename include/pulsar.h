@@ -130,12 +130,13 @@ int pulsar_select(const pulsar_geom* g, const int32_t* tok, int32_t* sel,
  *   tok   [L] int32 token ids (not read by UNIFORM and EVEN)
  *   sel   [N][kept] int32 out
  *   seed  UNIFORM only
- *   ws    at least pulsar_workspace_bytes(g, NULL) bytes; its first word is the
+ *   ws    at least pulsar_workspace_bytes(g, NULL) bytes (it holds 36 bytes of
+ *         scratch per chunk for these methods); its first word is the
  *         status word, set to 1 when a token id lies outside [0, vocab_size)
  *         (MAX_IDF, MEAN_IDF and ENTROPY read the ids)
  * Errors: PULSAR_EINVAL (also an unknown method), PULSAR_EWORKSPACE,
  * PULSAR_EUNSUPPORTED (mean IDF with N^chunk >= 2^256, entropy with
- * chunk^chunk >= 2^256, or more than 4096 chunks per block), PULSAR_EHIP. */
+ * chunk^chunk >= 2^256), PULSAR_EHIP. */
 #define PULSAR_SELECT_MAX_IDF 0
 #define PULSAR_SELECT_MEAN_IDF 1
 #define PULSAR_SELECT_ENTROPY 2

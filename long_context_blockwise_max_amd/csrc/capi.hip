@@ -62,9 +62,11 @@ int check_pair(const pulsar_geom* g, const pulsar_attn* a) {
   return PULSAR_OK;
 }
 
-// select + phase 1 workspace: status word | df | rotated q | prefix lists | work order
+// select + phase 1 workspace: status word | df | chunk keys | chunk ranks |
+// rotated q | prefix lists | work order (keys and ranks serve the selection
+// methods other than Max-IDF)
 struct Layout {
-  size_t status, df, q_rot, lists, order, total;
+  size_t status, df, keys, ranks, q_rot, lists, order, total;
 };
 
 Layout layout(const pulsar_geom* g, const pulsar_attn* a) {
@@ -74,6 +76,11 @@ Layout layout(const pulsar_geom* g, const pulsar_attn* a) {
   off += kAlign;
   l.df = off;
   off = align_up(off + (size_t)g->vocab_size * 4);
+  const size_t chunks = (size_t)g->n_blocks * (g->block_size / g->chunk_size);
+  l.keys = off;
+  off = align_up(off + chunks * 32);
+  l.ranks = off;
+  off = align_up(off + chunks * 4);
   const int64_t L = (int64_t)g->n_blocks * g->block_size;
   l.q_rot = l.lists = l.order = off;
   if (a) {
@@ -171,8 +178,6 @@ int pulsar_select_method(const pulsar_geom* g, int32_t method, uint64_t seed, co
   const bool reads_tokens = method == PULSAR_SELECT_MEAN_IDF || method == PULSAR_SELECT_ENTROPY;
   if (reads_tokens && !aligned16(tok)) return PULSAR_EINVAL;
   if (kept > 0 && !aligned16(sel)) return PULSAR_EINVAL;
-  const int64_t n_chunks = g->block_size / g->chunk_size;
-  if (method != PULSAR_SELECT_EVEN && n_chunks > 4096) return PULSAR_EUNSUPPORTED;  // LDS keys
   // the exact order keys are products over a chunk's positions held in 256 bits
   if (method == PULSAR_SELECT_MEAN_IDF && g->chunk_size * log2((double)g->n_blocks) >= 255.5)
     return PULSAR_EUNSUPPORTED;
@@ -184,8 +189,11 @@ int pulsar_select_method(const pulsar_geom* g, int32_t method, uint64_t seed, co
   char* w = static_cast<char*>(ws);
   int32_t* status = reinterpret_cast<int32_t*>(w + l.status);
   int32_t* dfp = reinterpret_cast<int32_t*>(w + l.df);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(w + l.keys);
+  int32_t* ranks = reinterpret_cast<int32_t*>(w + l.ranks);
   return launch_select_method(method, seed, tok, g->n_blocks, g->block_size, g->chunk_size, kept,
-                              g->vocab_size, sel, dfp, status, as_stream(stream)) == 0
+                              g->vocab_size, sel, dfp, keys, ranks, status,
+                              as_stream(stream)) == 0
              ? PULSAR_OK
              : PULSAR_EHIP;
 }

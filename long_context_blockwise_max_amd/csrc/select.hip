@@ -171,11 +171,17 @@ int launch_select(const int32_t* tok, int32_t n_blocks, int32_t block_size, int3
 // chunk, so both fall as an integer product over the chunk's positions rises.
 // Each chunk's product is formed exactly in 256 bits (the launcher checks that
 // it fits), and a chunk is kept when fewer than k chunks of its block have a
-// smaller product, or an equal product and a lower index: the same ties as Max-IDF,
-// decided exactly.  One workgroup per block; the keys sit in LDS and every
-// thread ranks its chunks against all of them.
+// smaller product, or an equal product and a lower index: the same ties as
+// Max-IDF, decided exactly.  Three launches, spread over all chunk pairs:
+//   select_keys     one thread per chunk: its key into the workspace, its rank
+//                   counter zeroed
+//   select_rank     one wave per (block, 64 chunks, 64 other chunks): the other
+//                   chunks' keys through LDS, each lane counts the ones that beat
+//                   its chunk and adds the count to the chunk's rank
+//   select_compact  one workgroup per block: chunks with rank < k, in order
 
 constexpr int kKeyLimbs = 8;   // 256-bit keys, little-endian 32-bit limbs
+constexpr int kRankTile = 64;  // chunks per side of a select_rank tile
 
 __device__ __forceinline__ void key_mul(uint32_t (&k)[kKeyLimbs], uint32_t f) {
   uint64_t carry = 0;
@@ -194,7 +200,45 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t n) {
   return z ^ (z >> 31);
 }
 
-// true when key a (registers) is smaller than key b (LDS)
+template <int METHOD>   // 1 mean IDF, 2 entropy, 3 uniform
+__global__ void __launch_bounds__(256) select_keys(
+    const int32_t* __restrict__ tok, const int32_t* __restrict__ df, int32_t n_blocks,
+    int32_t block_size, int32_t chunk_size, int32_t vocab, uint64_t seed,
+    uint32_t* __restrict__ keys, int32_t* __restrict__ ranks, int32_t* __restrict__ status) {
+  const int n_chunks = block_size / chunk_size;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)n_blocks * n_chunks) return;
+  uint32_t k[kKeyLimbs] = {1u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  if constexpr (METHOD == 3) {
+    const uint64_t z = splitmix64(seed, (uint64_t)idx + 1);   // counter j * n_chunks + c + 1
+    k[0] = (uint32_t)z;
+    k[1] = (uint32_t)(z >> 32);
+  } else {
+    const int j = (int)(idx / n_chunks), c = (int)(idx % n_chunks);
+    const int32_t* ct = tok + (int64_t)j * block_size + (int64_t)c * chunk_size;
+    bool bad = false;
+    for (int e = 0; e < chunk_size; ++e) {
+      const int32_t id = ct[e];
+      const bool in_range = id >= 0 && id < vocab;
+      bad |= !in_range;
+      uint32_t f;
+      if constexpr (METHOD == 1) {
+        f = in_range ? (uint32_t)df[id] : (uint32_t)n_blocks;
+      } else {
+        f = 0;
+        for (int e2 = 0; e2 < chunk_size; ++e2) f += ct[e2] == id;
+      }
+      key_mul(k, f);
+    }
+    if (bad) atomicOr(status, 1);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(keys + idx * kKeyLimbs);
+  dst[0] = u32x4{k[0], k[1], k[2], k[3]};
+  dst[1] = u32x4{k[4], k[5], k[6], k[7]};
+  ranks[idx] = 0;
+}
+
+// -1, 0, 1 as key a (registers) is smaller than, equal to or larger than key b
 __device__ __forceinline__ int key_cmp(const uint32_t (&a)[kKeyLimbs], const uint32_t* b) {
 #pragma unroll
   for (int i = kKeyLimbs - 1; i >= 0; --i) {
@@ -204,59 +248,47 @@ __device__ __forceinline__ int key_cmp(const uint32_t (&a)[kKeyLimbs], const uin
   return 0;
 }
 
-template <int METHOD>   // 1 mean IDF, 2 entropy, 3 uniform
-__global__ void __launch_bounds__(kSelThreads) select_keyed(
-    const int32_t* __restrict__ tok, const int32_t* __restrict__ df, int32_t n_blocks,
-    int32_t block_size, int32_t chunk_size, int32_t kept, int32_t vocab, uint64_t seed,
-    int32_t* __restrict__ sel, int32_t* __restrict__ status) {
-  extern __shared__ uint32_t keys[];   // [n_chunks][kKeyLimbs]
-  __shared__ int wave_tot[kSelWaves];
-  const int n_chunks = block_size / chunk_size;
-  const int j = blockIdx.x;
-  const int32_t* t = tok + (int64_t)j * block_size;
-  bool bad = false;
-  for (int c = threadIdx.x; c < n_chunks; c += blockDim.x) {
-    uint32_t k[kKeyLimbs] = {1u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    if constexpr (METHOD == 3) {
-      const uint64_t z = splitmix64(seed, (uint64_t)j * n_chunks + c + 1);
-      k[0] = (uint32_t)z;
-      k[1] = (uint32_t)(z >> 32);
-    } else {
-      const int32_t* ct = t + c * chunk_size;
-      for (int e = 0; e < chunk_size; ++e) {
-        const int32_t id = ct[e];
-        const bool in_range = id >= 0 && id < vocab;
-        bad |= !in_range;
-        uint32_t f;
-        if constexpr (METHOD == 1) {
-          f = in_range ? (uint32_t)df[id] : (uint32_t)n_blocks;
-        } else {
-          f = 0;
-          for (int e2 = 0; e2 < chunk_size; ++e2) f += ct[e2] == id;
-        }
-        key_mul(k, f);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kKeyLimbs; ++i) keys[c * kKeyLimbs + i] = k[i];
+__global__ void __launch_bounds__(kRankTile) select_rank(const uint32_t* __restrict__ keys,
+                                                         int32_t n_chunks, int32_t tiles,
+                                                         int32_t* __restrict__ ranks) {
+  __shared__ uint32_t other[kRankTile * kKeyLimbs];
+  const int per_block = tiles * tiles;
+  const int j = blockIdx.x / per_block;
+  const int r = blockIdx.x % per_block;
+  const int c = (r / tiles) * kRankTile + threadIdx.x;       // this lane's chunk
+  const int c2_0 = (r % tiles) * kRankTile;                 // the other chunks
+  const uint32_t* kb = keys + (int64_t)j * n_chunks * kKeyLimbs;
+  const int n_other = min(kRankTile, n_chunks - c2_0);
+  if ((int)threadIdx.x < n_other) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(kb + (int64_t)(c2_0 + threadIdx.x) * kKeyLimbs);
+    u32x4* dst = reinterpret_cast<u32x4*>(other + threadIdx.x * kKeyLimbs);
+    dst[0] = src[0];
+    dst[1] = src[1];
   }
-  if (bad) atomicOr(status, 1);
   __syncthreads();
+  if (c >= n_chunks) return;
+  uint32_t k[kKeyLimbs];
+  const u32x4* mine = reinterpret_cast<const u32x4*>(kb + (int64_t)c * kKeyLimbs);
+  const u32x4 lo = mine[0], hi = mine[1];
+  k[0] = lo[0]; k[1] = lo[1]; k[2] = lo[2]; k[3] = lo[3];
+  k[4] = hi[0]; k[5] = hi[1]; k[6] = hi[2]; k[7] = hi[3];
+  int better = 0;
+  for (int u = 0; u < n_other; ++u) {
+    const int cmp = key_cmp(k, other + u * kKeyLimbs);
+    better += (cmp > 0) || (cmp == 0 && c2_0 + u < c);
+  }
+  if (better) atomicAdd(&ranks[(int64_t)j * n_chunks + c], better);
+}
+
+__global__ void __launch_bounds__(kSelThreads) select_compact(const int32_t* __restrict__ ranks,
+                                                              int32_t n_chunks, int32_t kept,
+                                                              int32_t* __restrict__ sel) {
+  __shared__ int wave_tot[kSelWaves];
+  const int j = blockIdx.x;
   int out_base = 0;
   for (int base = 0; base < n_chunks; base += kSelThreads) {
     const int c = base + threadIdx.x;
-    bool take = false;
-    if (c < n_chunks) {
-      uint32_t k[kKeyLimbs];
-#pragma unroll
-      for (int i = 0; i < kKeyLimbs; ++i) k[i] = keys[c * kKeyLimbs + i];
-      int better = 0;
-      for (int c2 = 0; c2 < n_chunks && better < kept; ++c2) {
-        const int r = key_cmp(k, keys + c2 * kKeyLimbs);
-        better += (r > 0) || (r == 0 && c2 < c);
-      }
-      take = better < kept;
-    }
+    const bool take = c < n_chunks && ranks[(int64_t)j * n_chunks + c] < kept;
     int out_tot;
     const int slot = out_base + wg_exclusive_count(take, wave_tot, &out_tot);
     if (take) sel[(int64_t)j * kept + slot] = c;
@@ -274,7 +306,8 @@ __global__ void __launch_bounds__(256) select_even(int32_t n_blocks, int32_t n_c
 
 int launch_select_method(int32_t method, uint64_t seed, const int32_t* tok, int32_t n_blocks,
                          int32_t block_size, int32_t chunk_size, int32_t kept, int32_t vocab,
-                         int32_t* sel, int32_t* df, int32_t* status, hipStream_t stream) {
+                         int32_t* sel, int32_t* df, uint32_t* keys, int32_t* ranks,
+                         int32_t* status, hipStream_t stream) {
   const int n_chunks = block_size / chunk_size;
   // the status word (and df, for mean IDF) start at zero
   const int32_t clear_n = method == 1 ? vocab : 0;
@@ -296,20 +329,22 @@ int launch_select_method(int32_t method, uint64_t seed, const int32_t* tok, int3
     hipLaunchKernelGGL(select_df, dim3(n_blocks), dim3(1024), bitmap_bytes, stream, tok,
                        block_size, vocab, df, status);
   }
-  const size_t lds = (size_t)n_chunks * kKeyLimbs * 4;
-  auto go = [&](const void* fn, auto kernel) {
-    if (lds > 65536 &&
-        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return -3;
-    hipLaunchKernelGGL(kernel, dim3(n_blocks), dim3(kSelThreads), lds, stream, tok, df, n_blocks,
-                       block_size, chunk_size, kept, vocab, seed, sel, status);
-    return 0;
-  };
-  int rc = 0;
-  if (method == 1) rc = go(reinterpret_cast<const void*>(&select_keyed<1>), select_keyed<1>);
-  else if (method == 2) rc = go(reinterpret_cast<const void*>(&select_keyed<2>), select_keyed<2>);
-  else rc = go(reinterpret_cast<const void*>(&select_keyed<3>), select_keyed<3>);
-  if (rc) return rc;
+  const int64_t total = (int64_t)n_blocks * n_chunks;
+  const dim3 kgrid((unsigned)((total + 255) / 256));
+  if (method == 1)
+    hipLaunchKernelGGL(select_keys<1>, kgrid, dim3(256), 0, stream, tok, df, n_blocks, block_size,
+                       chunk_size, vocab, seed, keys, ranks, status);
+  else if (method == 2)
+    hipLaunchKernelGGL(select_keys<2>, kgrid, dim3(256), 0, stream, tok, df, n_blocks, block_size,
+                       chunk_size, vocab, seed, keys, ranks, status);
+  else
+    hipLaunchKernelGGL(select_keys<3>, kgrid, dim3(256), 0, stream, tok, df, n_blocks, block_size,
+                       chunk_size, vocab, seed, keys, ranks, status);
+  const int tiles = (n_chunks + kRankTile - 1) / kRankTile;
+  hipLaunchKernelGGL(select_rank, dim3((unsigned)((int64_t)n_blocks * tiles * tiles)),
+                     dim3(kRankTile), 0, stream, keys, n_chunks, tiles, ranks);
+  hipLaunchKernelGGL(select_compact, dim3(n_blocks), dim3(kSelThreads), 0, stream, ranks, n_chunks,
+                     kept, sel);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

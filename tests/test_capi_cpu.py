@@ -103,7 +103,6 @@ def test_select_method_rejects_bad_arguments():
     # exact order keys must fit 256 bits: N^chunk for mean IDF, chunk^chunk for entropy
     assert sm(geom(n_blocks=300, block_size=1024, budget_chunks=4), 1) == B.PULSAR_EUNSUPPORTED
     assert sm(geom(chunk_size=64), 2) == B.PULSAR_EUNSUPPORTED
-    assert sm(geom(block_size=65536, chunk_size=8, budget_chunks=4), 3) == B.PULSAR_EUNSUPPORTED  # > 4096 chunks
 
 
 @needs_lib
