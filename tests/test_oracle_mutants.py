@@ -290,3 +290,74 @@ def test_prefix_row_without_itself_is_caught(monkeypatch):
     _caught(monkeypatch, A.prefix_rows, bad,
             [TA.test_prefix_rows_of_a_contiguous_prefix_are_textbook_causal_attention,
              TA.test_prefix_rows_gather_equals_multiplicity_bias_dense])
+
+
+# ------------------------------------------------------ selection methods
+from oracle import selection_variants as SV
+from tests import test_oracle_selection_variants as TV
+
+VARIANT_PINS = [(TV.test_mean_idf_exact_order_equals_the_float_definition, (0,)),
+                (TV.test_mean_idf_exact_order_equals_the_float_definition, (4,)),
+                TV.test_mean_idf_loses_the_answer_of_figure2,
+                (TV.test_entropy_exact_order_equals_scipy_entropy, (0,)),
+                (TV.test_entropy_exact_order_equals_scipy_entropy, (4,)),
+                TV.test_entropy_closed_forms,
+                TV.test_uniform_selection_is_uniform_and_seeded,
+                TV.test_even_spacing_closed_form]
+
+
+def _replace_variant(monkeypatch, original, replacement):
+    for mod in (SV, TV):
+        for name, val in list(vars(mod).items()):
+            if val is original:
+                monkeypatch.setattr(mod, name, replacement)
+
+
+def _caught_variant(monkeypatch, original, replacement):
+    _replace_variant(monkeypatch, original, replacement)
+    assert _failing(VARIANT_PINS), f"no pin caught the planted mistake in {original.__name__}"
+
+
+def test_mean_idf_key_of_the_maximum_df_is_caught(monkeypatch):
+    orig = SV.mean_idf_keys
+
+    def bad(tokens, n_blocks, block_size, chunk_size, vocab_size):
+        # the product replaced by the largest df: the chunk's most common token
+        tokens = np.asarray(tokens)
+        df = S.document_frequency(tokens, n_blocks, block_size, vocab_size)
+        n_chunks = block_size // chunk_size
+        return [[max(int(df[t]) for t in tokens[j * block_size + c * chunk_size:
+                                                   j * block_size + (c + 1) * chunk_size])
+                 for c in range(n_chunks)] for j in range(n_blocks)]
+    _caught_variant(monkeypatch, orig, bad)
+
+
+def test_entropy_key_of_distinct_count_is_caught(monkeypatch):
+    def bad(tokens, n_blocks, block_size, chunk_size):
+        # fewer distinct ids as the better chunk: the order inverted
+        tokens = np.asarray(tokens)
+        n_chunks = block_size // chunk_size
+        return [[len(set(tokens[j * block_size + c * chunk_size:
+                                j * block_size + (c + 1) * chunk_size].tolist()))
+                 for c in range(n_chunks)] for j in range(n_blocks)]
+    _caught_variant(monkeypatch, SV.entropy_keys, bad)
+
+
+def test_uniform_keys_without_the_block_in_the_counter_is_caught(monkeypatch):
+    def bad(seed, n_blocks, n_chunks):
+        # every block draws the same counters
+        return [[SV.splitmix64(seed, c + 1) for c in range(n_chunks)] for _ in range(n_blocks)]
+    _caught_variant(monkeypatch, SV.uniform_keys, bad)
+
+
+def test_even_spacing_off_by_half_is_caught(monkeypatch):
+    orig = SV.select_variant
+
+    def bad(method, tokens, n_blocks, block_size, chunk_size, budget_chunks, vocab_size, seed=0):
+        if method != "even":
+            return orig(method, tokens, n_blocks, block_size, chunk_size, budget_chunks, vocab_size, seed)
+        n_chunks = block_size // chunk_size
+        k = min(budget_chunks, n_chunks)
+        row = [min(n_chunks - 1, (2 * m + 1) * n_chunks // (2 * k)) for m in range(k)]
+        return np.array([row] * n_blocks, dtype=np.int64).reshape(n_blocks, k)
+    _caught_variant(monkeypatch, orig, bad)
