@@ -213,6 +213,27 @@ __global__ void __launch_bounds__(256) select_keys(
     const uint64_t z = splitmix64(seed, (uint64_t)idx + 1);   // counter j * n_chunks + c + 1
     k[0] = (uint32_t)z;
     k[1] = (uint32_t)(z >> 32);
+  } else if (METHOD == 2 && chunk_size == 32) {
+    // the method's 32-token chunks: the ids in registers, counted pairwise there
+    const int j = (int)(idx / n_chunks), c = (int)(idx % n_chunks);
+    const int32_t* ct = tok + (int64_t)j * block_size + (int64_t)c * 32;
+    int32_t ids[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const u32x4 x = reinterpret_cast<const u32x4*>(ct)[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ids[4 * q + e] = (int32_t)x[e];
+    }
+    bool bad = false;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      bad |= !(ids[e] >= 0 && ids[e] < vocab);
+      uint32_t f = 0;
+#pragma unroll
+      for (int e2 = 0; e2 < 32; ++e2) f += ids[e2] == ids[e];
+      key_mul(k, f);
+    }
+    if (bad) atomicOr(status, 1);
   } else {
     const int j = (int)(idx / n_chunks), c = (int)(idx % n_chunks);
     const int32_t* ct = tok + (int64_t)j * block_size + (int64_t)c * chunk_size;
