@@ -103,3 +103,31 @@ def test_decode_of_the_query_tokens_is_the_query_phase():
                  max_abs=1e-5, mean_abs=1e-6)
     assert_close(lse.cpu().numpy(), path.lse_q.cpu().numpy().astype(np.float64), "decode == query LSE",
                  max_abs=1e-5, mean_abs=1e-6)
+
+
+def test_generation_at_128k_matches_the_oracle():
+    """Two generated tokens over the full 128K workload's retained shards (all 32
+    heads against a masked dense softmax over 131072 + 66 keys)."""
+    torch = torch_cuda()
+    w = W.WORKLOADS["128k"]
+    case = Case(w, extra_seqs=False)
+    case.run()
+    gq, gk, gv = W.generated(w, 2)
+    path = case.path
+    path.decode_setup(2)
+    kc, vc = _retained(case, 0)
+    for step in range(2):
+        _bits_to(path.q1, gq[step])
+        _bits_to(path.k1, gk[step])
+        _bits_to(path.v1, gv[step])
+        log(f"[decode] 128k: step {step}")
+        path.decode_step()
+        torch.cuda.synchronize()
+        ks = np.concatenate([case.kq[0], gk[:step + 1, 0, 0]], axis=0)
+        vs = np.concatenate([case.vq[0], gv[:step + 1, 0, 0]], axis=0)
+        want_o, want_lse = OA.dense_decode_attention(
+            W.bf16_bits_to_f64(gq[step, 0]), kc, vc, W.bf16_bits_to_f64(ks),
+            W.bf16_bits_to_f64(vs), w.context_len, w.rope_base)
+        assert_close(path.o1.cpu().numpy()[0], want_o, f"128k decode step {step} O")
+        assert_close(path.lse1.cpu().numpy()[0], want_lse, f"128k decode step {step} LSE",
+                     max_abs=LSE_ABS, mean_abs=LSE_ABS)

@@ -43,7 +43,7 @@ def test_prefix_rows_small_all_rows(name):
     assert_close(got, want, f"{name} prefix rows ({n} rows x {w.n_q_heads} heads)")
 
 
-@pytest.mark.parametrize("name", ["128k", "32k"])
+@pytest.mark.parametrize("name", ["128k", "32k", "128k_star", "512k"])
 def test_prefix_rows_full_size_sampled(name):
     torch_cuda()
     w = W.WORKLOADS[name]
@@ -52,8 +52,9 @@ def test_prefix_rows_full_size_sampled(name):
     pre = _prefix_last(case)
     assert n == len(pre)
     rng = np.random.default_rng(w.seed)
-    rows = sorted(set([0, 1, 31, 32, 63, 64, w.sink_size - 1, w.sink_size, n - 65, n - 64, n - 1]
-                      + [int(x) for x in rng.choice(n, size=8, replace=False)]))
+    rows = sorted(set(r for r in [0, 1, 31, 32, 63, 64, w.sink_size - 1, w.sink_size, n - 65,
+                                  n - 64, n - 1] + [int(x) for x in rng.choice(n, size=8, replace=False)]
+                      if 0 <= r < n))
     log(f"[prefix] {name}: {n} prefix rows, checking {len(rows)}")
     import torch
     got = case.path.o_prefix.index_select(0, torch.tensor(rows, device="cuda")).cpu().numpy()
