@@ -216,6 +216,83 @@ __device__ __forceinline__ void flash_sub(const char* stage, int kt,
   }
 }
 
+// The three steps of flash_sub for one query tile, taken apart so that the
+// Phase-1 loop can issue the next tile's loads between them.
+template <int D>
+__device__ __forceinline__ void sub_qk(const char* stage, int kt, const bf16x8 (&q)[D / 16],
+                                       f32x16& s) {
+  using KTl = KTile<D>;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int krow = kt * 32 + key_perm(lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 a = *(const bf16x8*)(stage + KTl::off(krow, 16 * ks + 8 * half));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[ks], s, 0, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void sub_softmax(f32x16& s, FlashState<D, 1>& st, float sl2, int lim,
+                                            bf16x8 (&p)[2]) {
+  const int half = (threadIdx.x & 63) >> 5;
+  if (__ballot(lim < 32)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (reg_key(r, half) >= lim) s[r] = -INFINITY;
+  }
+  float sum;
+  softmax_p<1>(s, sl2, st.m[0], p, sum);
+  if (__ballot(!(sum <= kRescaleBound))) {
+    float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_new = fmaxf(st.m[0], mx * sl2);
+    const float alpha = __builtin_amdgcn_exp2f(st.m[0] - m_new);
+    st.m[0] = m_new;
+    st.l[0] *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[dt][0][r] *= alpha;
+    softmax_p<1>(s, sl2, st.m[0], p, sum);
+  }
+  st.l[0] += sum;
+}
+
+template <int D>
+__device__ __forceinline__ void sub_pv(const char* stage, int kt, const bf16x8 (&p)[2],
+                                       FlashState<D, 1>& st) {
+  using VTl = VTile<D>;
+  const char* Vt = stage + KTile<D>::BYTES;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int lr = lane & 31;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const bf16x8 a = *(const bf16x8*)(Vt + VTl::off(dt * 32 + lr, kt * 4 + 2 * hh + half));
+      st.o[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[hh], st.o[dt][0], 0, 0, 0);
+    }
+  }
+}
+
+// Raw byte-addressed buffer resource over `bytes` bytes at `base`: loads at
+// offsets past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane at base + soff + voff into LDS (buffer_load_dwordx4 ... lds).
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                          char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PULSAR_LDS void*)lds, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ void dma16(const uint16_t* src, char* lds) {
   __builtin_amdgcn_global_load_lds((const void*)src, (PULSAR_LDS void*)lds, 16, 0, 0);
 }
@@ -440,7 +517,6 @@ phase1_kernel(P1Args a) {
   const int64_t own_v = ((int64_t)i * a.hkv) * D * a.b + vb_; // V column of own key 0
   const uint16_t* kbase = a.kc;
   const uint16_t* vbase = a.vc;
-  const int64_t v_ld = a.b;
 
   bf16x8 qf[NQ][D / 16];
   {
@@ -458,75 +534,117 @@ phase1_kernel(P1Args a) {
   FlashState<D, NQ> st;
   flash_init(st);
 
-  // Staging addresses.  A prefix tile takes its key positions from the prefix
-  // lists; the list entries of tile t+1 are loaded one iteration ahead (raw
-  // registers), so the barrier's wait already covers them and no DMA waits on a
-  // list load.  Keys past the list read the list's first key (masked below).
-  constexpr int KNI = KTile<D>::NI, VNI = VTile<D>::NI;
-  int32_t rk[KNI], rv[VNI];
+  // Staging, through buffer resources over the caches (byte offsets fit in 32
+  // bits: L Hkv d < 2^31).  Every 8-entry run of a prefix list is 8 consecutive
+  // cache rows (sink, chunk and block sizes are multiples of 8), and the K rows a
+  // wave stages per tile are one such run: a K tile needs one list entry per
+  // wave (a scalar load), and a lane's source offset is a constant of the lane
+  // plus a per-wave base.  A V lane stages the 8-key run `v_run` of its d-row,
+  // whose list entry it loads one tile ahead.  List entries past the list read
+  // as 0 (the buffer resource ends with the list), which is a readable key, and
+  // own-block runs past the block's b keys (a ragged last tile) read key 0.
+  using KTl = KTile<D>;
+  using VTl = VTile<D>;
+  constexpr int KNI = KTl::NI, VNI = VTl::NI;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const uint32_t kbytes = (uint32_t)a.n_blocks * a.hkv * a.b * D * 2;   // < 2^32 (L Hkv d < 2^31)
+  const __amdgpu_buffer_rsrc_t krs = raw_rsrc(kbase, kbytes);
+  const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(vbase, kbytes);
+  const int n_list = PR ? n_rows : P;                  // entries of this block's list
+  const __amdgpu_buffer_rsrc_t vls = raw_rsrc(vcol, (uint32_t)n_list * 4);
+  const __attribute__((address_space(4))) int32_t* krow_s =
+      (const __attribute__((address_space(4))) int32_t*)krow;
+  uint32_t k_voff[KNI], v_voff[VNI], vl_voff[VNI];
+#pragma unroll
+  for (int x = 0; x < KNI; ++x) {
+    const int row = (wv * KNI + x) * KTl::RPI + lane / KTl::CPR;   // tile row (0..63)
+    const int c = (lane % KTl::CPR) ^ KTl::sw(row);
+    k_voff[x] = (uint32_t)((row - 8 * wv) * D + 8 * c) * 2;
+  }
+  int v_run[VNI];
+#pragma unroll
+  for (int y = 0; y < VNI; ++y) {
+    const int dv = (wv * VNI + y) * VTl::RPI + lane / VTl::CPR;   // d-row (0..D-1)
+    v_run[y] = (lane % VTl::CPR) ^ VTl::sw(dv);                   // 8-key run of the tile
+    v_voff[y] = (uint32_t)dv * (uint32_t)a.b * 2;
+    vl_voff[y] = (uint32_t)(8 * v_run[y]) * 4;
+  }
+  int32_t k_ent = 0;        // list entry of this wave's K run of the next tile to stage
+  int32_t rv[VNI];          // list entries of this lane's V runs of that tile
   auto fetch_raw = [&](int t) __attribute__((always_inline)) {
-    if (PR) {   // every tile through the list, entries past this tile's rows clamped
+    if (PR || t < n_pre) {
+      const int e = t * KT + 8 * wv;
+      k_ent = krow_s[e < n_list ? e : 0];
 #pragma unroll
-      for (int x = 0; x < KNI; ++x) {
-        const int e = t * KT + staged_k_row<D>(x);
-        rk[x] = krow[e < own_end ? e : 0];
-      }
-#pragma unroll
-      for (int x = 0; x < VNI; ++x) {
-        const int e = t * KT + 8 * staged_v_chunk<D>(x);
-        rv[x] = vcol[e < own_end ? e : 0];
-      }
-    } else if (t < n_pre) {
-#pragma unroll
-      for (int x = 0; x < KNI; ++x) {
-        const int e = t * KT + staged_k_row<D>(x);
-        rk[x] = krow[e < P ? e : 0];
-      }
-#pragma unroll
-      for (int x = 0; x < VNI; ++x) {
-        const int e = t * KT + 8 * staged_v_chunk<D>(x);
-        rv[x] = vcol[e < P ? e : 0];
-      }
-    } else {
-#pragma unroll
-      for (int x = 0; x < KNI; ++x) {
-        const int kk = (t - n_pre) * KT + staged_k_row<D>(x);
-        rk[x] = kk < own_end ? kk : 0;
-      }
-#pragma unroll
-      for (int x = 0; x < VNI; ++x) {
-        const int kk = (t - n_pre) * KT + 8 * staged_v_chunk<D>(x);
-        rv[x] = kk < own_end ? kk : 0;
-      }
+      for (int y = 0; y < VNI; ++y)
+        rv[y] = __builtin_amdgcn_raw_buffer_load_b32(vls, vl_voff[y] + (uint32_t)t * (KT * 4), 0, 0);
     }
   };
-  auto src_of = [&](int t) __attribute__((always_inline)) {
-    TileSrc<D> sr;
+  // part 0: K only, 1: V only, 2: both
+  auto stage = [&](int t, char* dst, int part) __attribute__((always_inline)) {
     const bool pre = PR || t < n_pre;
+    uint32_t ks, vs;
+    bool v_const = true;
+    if (pre) {
+      ks = (uint32_t)(kb_ + k_ent) * (D * 2);
+      vs = (uint32_t)vb_ * 2;
+      v_const = false;
+    } else {
+      int kk = (t - n_pre) * KT + 8 * wv;
+      kk = kk < a.b ? kk : 0;
+      ks = (uint32_t)(own_k + kk) * (D * 2);
+      v_const = (t - n_pre + 1) * KT <= a.b;
+      vs = (uint32_t)(own_v + (v_const ? (t - n_pre) * KT : 0)) * 2;
+    }
+    if (part != 1) {
 #pragma unroll
-    for (int x = 0; x < KNI; ++x) sr.k[x] = ((pre ? kb_ : own_k) + rk[x]) * D;
+      for (int x = 0; x < KNI; ++x) dma16_buf(krs, k_voff[x], ks, dst + (wv * KNI + x) * 1024);
+    }
+    if (part == 0) return;
 #pragma unroll
-    for (int x = 0; x < VNI; ++x) sr.v[x] = (pre ? vb_ : own_v) + rv[x];
-    return sr;
+    for (int y = 0; y < VNI; ++y) {
+      uint32_t vo;
+      if (pre) {
+        vo = v_voff[y] + (uint32_t)rv[y] * 2;
+      } else if (v_const) {
+        vo = v_voff[y] + (uint32_t)(8 * v_run[y]) * 2;
+      } else {
+        const int col = (t - n_pre) * KT + 8 * v_run[y];   // ragged last tile
+        vo = v_voff[y] + (uint32_t)(col < a.b ? col : 0) * 2;
+      }
+      dma16_buf(vrs, vo, vs, dst + KTl::BYTES + (wv * VNI + y) * 1024);
+    }
   };
 
   fetch_raw(0);
-  stage_tile<D>(smem, kbase, vbase, v_ld, src_of(0));
+  stage(0, smem, 2);
   if (n_tiles > 1) fetch_raw(1);
   const float sl2 = a.scale_log2;
   for (int t = 0; t < n_tiles; ++t) {
     tile_barrier();  // tile t has landed for every wave; tile t-1 is no longer read
-    if (t + 1 < n_tiles) stage_tile<D>(smem + ((t + 1) & 1) * Stage<D>::BYTES, kbase, vbase, v_ld, src_of(t + 1));
-    if (t + 2 < n_tiles) fetch_raw(t + 2);
     const char* stg = smem + (t & 1) * Stage<D>::BYTES;
+    char* nxt = smem + ((t + 1) & 1) * Stage<D>::BYTES;
+    const bool more = t + 1 < n_tiles;
     const bool pre = t < n_pre;
+    // The loads of tile t+1 are issued in two parts, each behind the K.Q^T
+    // products of a subtile, so that a wave waiting to issue them has matrix
+    // work in flight.
 #pragma unroll
     for (int kt = 0; kt < NSUB; ++kt) {
       // prefix: every listed key is visible; own block: keys up to the row (causal)
       const int k1 = (pre ? t : t - n_pre) * KT + kt * 32;
       const int lim = pre ? P - k1 : min(r0 + lr - k1 + 1, own_end - k1);
-      if (!__ballot(lim > 0)) break;   // past the list, or above this wave's diagonal
-      flash_sub<D, NQ>(stg, kt, qf, st, sl2, lim);
+      const bool act = __ballot(lim > 0) != 0;   // else past the list, or above the diagonal
+      f32x16 s;
+      if (act) sub_qk<D>(stg, kt, qf[0], s);
+      if (more) stage(t + 1, nxt, kt);
+      if (kt == NSUB - 1 && t + 2 < n_tiles) fetch_raw(t + 2);
+      if (act) {
+        bf16x8 p[2];
+        sub_softmax<D>(s, st, sl2, lim, p);
+        sub_pv<D>(stg, kt, p, st);
+      }
     }
   }
 
