@@ -141,83 +141,11 @@ __device__ __forceinline__ void softmax_p(const f32x16& s, float sl2, float m, b
   sum = acc;
 }
 
-// One 32-key subtile `kt` (0 .. NSUB-1) of the staged tile.  Keys 0 .. lim-1 of the
-// subtile are visible to this lane's query row (lim >= 32: all of them); the
-// mask is applied only when some lane of the wave needs it.
-template <int D, int NQ>
-__device__ __forceinline__ void flash_sub(const char* stage, int kt,
-                                          const bf16x8 (&q)[NQ][D / 16],
-                                          FlashState<D, NQ>& st, float sl2, int lim) {
-  using KTl = KTile<D>;
-  using VTl = VTile<D>;
-  const char* Kt = stage;
-  const char* Vt = stage + KTl::BYTES;
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5;
-  const int lr = lane & 31;
-
-  f32x16 s[NQ];
-#pragma unroll
-  for (int qt = 0; qt < NQ; ++qt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[qt][r] = 0.f;
-  const int krow = kt * 32 + key_perm(lr);
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8 a = *(const bf16x8*)(Kt + KTl::off(krow, 16 * ks + 8 * half));
-#pragma unroll
-    for (int qt = 0; qt < NQ; ++qt)
-      s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[qt][ks], s[qt], 0, 0, 0);
-  }
-
-  bf16x8 p[NQ][2];
-#pragma unroll
-  for (int qt = 0; qt < NQ; ++qt) {
-    if (__ballot(lim < 32)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (reg_key(r, half) >= lim) s[qt][r] = -INFINITY;
-    }
-    // Fast path: p against the current reference maximum m, no max reduction.
-    // Every p stays <= 2^kRescaleSlack unless a score rose more than the slack
-    // above m, and then this lane's subtile sum exceeds 2^kRescaleSlack too (or
-    // is inf / nan), which sends the wave to the slow path: exact maximum,
-    // rescale of O and l, p recomputed.  The first subtile always takes it (m
-    // starts at -1e30).
-    float sum;
-    softmax_p<NQ>(s[qt], sl2, st.m[qt], p[qt], sum);
-    if (__ballot(!(sum <= kRescaleBound))) {
-      float mx = fmaxf(s[qt][0], s[qt][1]);
-#pragma unroll
-      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[qt][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(st.m[qt], mx * sl2);
-      const float alpha = __builtin_amdgcn_exp2f(st.m[qt] - m_new);
-      st.m[qt] = m_new;
-      st.l[qt] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st.o[dt][qt][r] *= alpha;
-      softmax_p<NQ>(s[qt], sl2, st.m[qt], p[qt], sum);
-    }
-    st.l[qt] += sum;
-  }
-
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const bf16x8 a = *(const bf16x8*)(Vt + VTl::off(dt * 32 + lr, kt * 4 + 2 * hh + half));
-#pragma unroll
-      for (int qt = 0; qt < NQ; ++qt)
-        st.o[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[qt][hh], st.o[dt][qt], 0, 0, 0);
-    }
-  }
-}
-
-// The three steps of flash_sub for one query tile, taken apart so that the
-// Phase-1 loop can issue the next tile's loads between them.
+// One 32-key subtile `kt` (0 .. NSUB-1) of a staged tile, in three steps (the
+// Phase-1 loop issues the next tile's loads between them):
+//   sub_qk       s = K . Q^T for the query tile's 32 rows
+//   sub_softmax  mask, p = exp2(s * sl2 - m) rounded to bf16, running sum and max
+//   sub_pv       O^T += V^T . P^T
 template <int D>
 __device__ __forceinline__ void sub_qk(const char* stage, int kt, const bf16x8 (&q)[D / 16],
                                        f32x16& s) {
@@ -234,6 +162,13 @@ __device__ __forceinline__ void sub_qk(const char* stage, int kt, const bf16x8 (
   }
 }
 
+// Keys 0 .. lim-1 of the subtile are visible to this lane's query row (lim >= 32:
+// all of them); the mask is applied only when some lane of the wave needs it.
+// Fast path: p against the current reference maximum m, no max reduction.  Every
+// p stays <= 2^kRescaleSlack unless a score rose more than the slack above m,
+// and then this lane's subtile sum exceeds 2^kRescaleSlack too (or is inf /
+// nan), which sends the wave to the slow path: exact maximum, rescale of O and
+// l, p recomputed.  The first subtile always takes it (m starts at -1e30).
 template <int D>
 __device__ __forceinline__ void sub_softmax(f32x16& s, FlashState<D, 1>& st, float sl2, int lim,
                                             bf16x8 (&p)[2]) {
@@ -993,7 +928,11 @@ phase2_kernel(P2Args a) {
       const int kb = k0 + t * KT + kt * 32;
       const int lim = self_part ? min(a.n_self - a.lq + tok - kb + 1, k1 - kb) : k1 - kb;
       if (!__ballot(lim > 0)) break;
-      flash_sub<D, NQ>(stg, kt, qf, st, sl2, lim);
+      f32x16 s;
+      bf16x8 p[2];
+      sub_qk<D>(stg, kt, qf[0], s);
+      sub_softmax<D>(s, st, sl2, lim, p);
+      sub_pv<D>(stg, kt, p, st);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may land after the workgroup ends
