@@ -173,14 +173,14 @@ template <int D>
 __device__ __forceinline__ void sub_softmax(f32x16& s, FlashState<D, 1>& st, float sl2, int lim,
                                             bf16x8 (&p)[2]) {
   const int half = (threadIdx.x & 63) >> 5;
-  if (__ballot(lim < 32)) {
+  if (__builtin_expect(__ballot(lim < 32) != 0, 0)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       if (reg_key(r, half) >= lim) s[r] = -INFINITY;
   }
   float sum;
   softmax_p<1>(s, sl2, st.m[0], p, sum);
-  if (__ballot(!(sum <= kRescaleBound))) {
+  if (__builtin_expect(__ballot(!(sum <= kRescaleBound)) != 0, 0)) {
     float mx = fmaxf(s[0], s[1]);
 #pragma unroll
     for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);

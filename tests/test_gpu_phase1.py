@@ -88,6 +88,13 @@ SMALL = {
     # budget above the chunk count: every chunk kept, so the sink tokens appear
     # twice in the prefix (once as the sink, once inside block 0's summary)
     "keep_all": dict(n_blocks=3, block_size=128, budget_chunks=100, n_planted=0),
+    # d = 128 with a block of 5.5 key tiles: the last own tile of the last KV head
+    # of the last block runs past the cache, and prefixes end on half tiles
+    "ragged_d128": dict(n_blocks=3, block_size=352, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                        budget_chunks=3, n_planted=0),
+    # d = 128, a 96-token sink: every prefix ends on a half tile
+    "sink96_d128": dict(n_blocks=4, block_size=192, sink_size=96, n_q_heads=4, n_kv_heads=2,
+                        head_dim=128, budget_chunks=1, n_planted=0),
 }
 
 
