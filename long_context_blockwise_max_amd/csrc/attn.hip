@@ -1,16 +1,18 @@
 // Flash-style attention kernels for Phase 1 (context encoding) and Phase 2
 // (query attention over retained shards) on gfx950.
 //
-// Both phases run one MFMA tile routine.  A workgroup is 8 waves, two per SIMD,
-// so that one wave's softmax (VALU) overlaps the other wave's matrix work.
-// All 8 waves share each KT-key K / V tile staged in LDS; each wave owns 32
-// query rows and keeps, per row, a running reference maximum, a running sum
-// and an fp32 output accumulator (online softmax, Milakov & Gimelshein, as the
-// Star Attention review names it).
+// Both phases run one MFMA tile routine.  A workgroup is 8 waves, two per SIMD
+// (Phase 1: 12 waves, three per SIMD, where the GQA group divides them), so
+// that one wave's softmax (VALU) can overlap another wave's matrix work.  All
+// waves share each KT-key K / V tile staged in LDS; each wave owns 32 query rows
+// and keeps, per row, a running reference maximum, a running sum and an fp32
+// output accumulator (online softmax, Milakov & Gimelshein, as the Star
+// Attention review names it).
 //
 // The contraction is done transposed so that every lane keeps one query row:
 //   S^T (keys x queries)  = K   . Q^T   v_mfma_f32_32x32x16_bf16: A = K rows from
-//                                       LDS, B = Q^T held in registers
+//                                       LDS, B = Q^T held in registers (or, with
+//                                       12 waves, read from LDS)
 //   O^T (d x queries)    += V^T . P^T   A = rows of the d-major V tile, B = P^T
 // In the 32x32 accumulator layout lane l holds column l % 32 (its query) and
 // 16 rows.  The K rows are fed in a permuted order (bits 2 and 3 of the row
@@ -19,10 +21,11 @@
 // and row sum need one exchange with lane l ^ 32 (v_permlane32_swap); the
 // rescale of O touches only the lane's own registers.
 //
-// Tiles are staged with direct global->LDS loads (global_load_lds_dwordx4), one
-// barrier per tile: two slots, one tile ahead, for Phase 1 and the Phase-2
-// query; four slots, three tiles ahead, for the Phase-2 decode form, which
-// streams from HBM with little work per tile.  The 16-byte chunks of every LDS
+// Tiles are staged with direct global->LDS loads (buffer_load_dwordx4 ... lds in
+// Phase 1, global_load_lds_dwordx4 in Phase 2), one barrier per tile: two slots,
+// one tile ahead, for Phase 1 and the Phase-2 query; four slots, three tiles
+// ahead, for the Phase-2 decode form, which streams from HBM with little work
+// per tile.  The 16-byte chunks of every LDS
 // row are XOR-swizzled so that fragment reads are bank-conflict free.
 //
 // Softmax runs in base 2: t = (q.k) * log2(e) / sqrt(d), p = exp2(t - m), with
@@ -41,6 +44,7 @@ constexpr int KT = 64;            // keys per LDS tile (one barrier per tile)
 constexpr int NSUB = KT / 32;     // 32-key subtiles per tile
 constexpr int NW = 8;             // waves per workgroup
 constexpr int NTHR = 64 * NW;
+constexpr int P1_WQ = 12;         // Phase-1 waves per workgroup when the GQA group allows (query rows in LDS)
 
 // K tile: KT key rows x D (row = 2D bytes)
 template <int D>
@@ -159,6 +163,23 @@ __device__ __forceinline__ void sub_qk(const char* stage, int kt, const bf16x8 (
   for (int ks = 0; ks < D / 16; ++ks) {
     const bf16x8 a = *(const bf16x8*)(stage + KTl::off(krow, 16 * ks + 8 * half));
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[ks], s, 0, 0, 0);
+  }
+}
+
+// sub_qk with the query rows staged in LDS (laid out like K tile rows).
+template <int D>
+__device__ __forceinline__ void sub_qk_lds(const char* stage, int kt, const char* qlds, f32x16& s) {
+  using KTl = KTile<D>;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int krow = kt * 32 + key_perm(lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 a = *(const bf16x8*)(stage + KTl::off(krow, 16 * ks + 8 * half));
+    const bf16x8 b = *(const bf16x8*)(qlds + KTl::off(lane & 31, 16 * ks + 8 * half));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s, 0, 0, 0);
   }
 }
 
@@ -412,11 +433,16 @@ struct P1Args {
 // come through the list, the mask is causal in list order, row tiles run longest
 // first, and a.n_rt counts the list's row tiles.
 
-template <int D, bool PR>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NTHR, NTHR), amdgpu_waves_per_eu(2, 2)))
+template <int D, bool PR, int NWV>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * NWV, 64 * NWV),
+                               amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
 phase1_kernel(P1Args a) {
   constexpr int NQ = 1;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * Stage<D>::BYTES];
+  // With 12 waves (3 per SIMD) the registers no longer hold the query rows: they
+  // sit in LDS behind the two slots (8 KB per wave at d = 128, 160 KB in all).
+  constexpr bool QL = NWV > NW;
+  constexpr int QBYTES = 32 * KTile<D>::ROWB;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * Stage<D>::BYTES + (QL ? NWV * QBYTES : 0)];
 
   const int hc_count = a.hkv * a.n_hs;
   const int hc = blockIdx.x % hc_count;
@@ -454,7 +480,27 @@ phase1_kernel(P1Args a) {
   const uint16_t* vbase = a.vc;
 
   bf16x8 qf[NQ][D / 16];
-  {
+  char* qlds = smem + 2 * Stage<D>::BYTES + (QL ? wave * QBYTES : 0);   // used when QL
+  if constexpr (QL) {
+    // Each lane of DMA x stages one 16-byte chunk of row x * RPI + lane / CPR;
+    // rows past the sequence read row r0 (finite; their outputs are not written).
+    using KTl = KTile<D>;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int x = 0; x < 32 / KTl::RPI; ++x) {
+      const int row = x * KTl::RPI + lane / KTl::CPR;
+      int r = r0 + row;
+      if (r >= n_rows) r = r0 < n_rows ? r0 : 0;
+      int64_t pos = (int64_t)i * a.b + r;
+      if constexpr (PR) {
+        const int64_t kr = krow[r];
+        const int64_t hb = (int64_t)a.hkv * a.b;
+        pos = (kr / hb) * a.b + kr % hb;
+      }
+      const int c = (lane % KTl::CPR) ^ KTl::sw(row);
+      dma16(a.q + (pos * a.hq + h) * D + 8 * c, qlds + x * 1024);
+    }
+  } else {
     const int r = r0 + lr;
     int64_t pos = (int64_t)i * a.b + r;
     if constexpr (PR) {
@@ -507,8 +553,9 @@ phase1_kernel(P1Args a) {
   }
   int32_t k_ent = 0;        // list entry of this wave's K run of the next tile to stage
   int32_t rv[VNI];          // list entries of this lane's V runs of that tile
+  const bool stager = !QL || wv < NW;   // the first 8 waves stage the tiles (one K run each)
   auto fetch_raw = [&](int t) __attribute__((always_inline)) {
-    if (PR || t < n_pre) {
+    if (stager && (PR || t < n_pre)) {
       const int e = t * KT + 8 * wv;
       k_ent = krow_s[e < n_list ? e : 0];
 #pragma unroll
@@ -518,6 +565,7 @@ phase1_kernel(P1Args a) {
   };
   // part 0: K only, 1: V only, 2: both
   auto stage = [&](int t, char* dst, int part) __attribute__((always_inline)) {
+    if (!stager) return;
     const bool pre = PR || t < n_pre;
     uint32_t ks, vs;
     bool v_const = true;
@@ -572,7 +620,10 @@ phase1_kernel(P1Args a) {
       const int lim = pre ? P - k1 : min(r0 + lr - k1 + 1, own_end - k1);
       const bool act = __ballot(lim > 0) != 0;   // else past the list, or above the diagonal
       f32x16 s;
-      if (act) sub_qk<D>(stg, kt, qf[0], s);
+      if (act) {
+        if constexpr (QL) sub_qk_lds<D>(stg, kt, qlds, s);
+        else sub_qk<D>(stg, kt, qf[0], s);
+      }
       if (more) stage(t + 1, nxt, kt);
       if (kt == NSUB - 1 && t + 2 < n_tiles) fetch_raw(t + 2);
       if (act) {
@@ -631,6 +682,15 @@ __global__ void __launch_bounds__(256) phase1_order(int32_t n_blocks, int32_t b,
   }
 }
 
+// phase1_kernel with the geometry's wave count
+template <int D, bool PR>
+void launch_p1(const Phase1Geometry& g, int grid, hipStream_t stream, const P1Args& a) {
+  if (g.rows_per_wg / 32 * g.heads_per_wg == P1_WQ)
+    hipLaunchKernelGGL((phase1_kernel<D, PR, P1_WQ>), dim3(grid), dim3(64 * P1_WQ), 0, stream, a);
+  else
+    hipLaunchKernelGGL((phase1_kernel<D, PR, NW>), dim3(grid), dim3(NTHR), 0, stream, a);
+}
+
 Phase1Geometry phase1_geometry(int32_t n_blocks, int32_t block_size, int32_t chunk_size,
                                int32_t kept, int32_t sink_size, int32_t n_q_heads,
                                int32_t n_kv_heads, int32_t head_dim) {
@@ -644,9 +704,12 @@ Phase1Geometry phase1_geometry(int32_t n_blocks, int32_t block_size, int32_t chu
   g.n_kv_heads = n_kv_heads;
   g.head_dim = head_dim;
   const int group = n_q_heads / n_kv_heads;
-  g.heads_per_wg = group >= NW ? NW : group;      // the 8 waves split as heads x 32-row groups
+  // 12 waves (3 per SIMD) where the heads x 32-row groups divide them (GQA group
+  // 1, 2, 3, 4, 6 or 12), else 8
+  const int waves = (group <= P1_WQ && P1_WQ % group == 0) ? P1_WQ : NW;
+  g.heads_per_wg = group >= waves ? waves : group;   // the waves split as heads x 32-row groups
   g.n_head_sub = group / g.heads_per_wg;
-  g.rows_per_wg = 32 * (NW / g.heads_per_wg);
+  g.rows_per_wg = 32 * (waves / g.heads_per_wg);
   g.n_row_tiles = (block_size + g.rows_per_wg - 1) / g.rows_per_wg;
   return g;
 }
@@ -702,10 +765,8 @@ int launch_phase1_attend(const Phase1Geometry& g, const uint16_t* q_rot, const u
   a.rpw = g.rows_per_wg;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.head_dim));
   const int grid = n_pairs * g.n_kv_heads * g.n_head_sub;
-  if (g.head_dim == 128)
-    hipLaunchKernelGGL((phase1_kernel<128, false>), dim3(grid), dim3(NTHR), 0, stream, a);
-  else
-    hipLaunchKernelGGL((phase1_kernel<64, false>), dim3(grid), dim3(NTHR), 0, stream, a);
+  if (g.head_dim == 128) launch_p1<128, false>(g, grid, stream, a);
+  else launch_p1<64, false>(g, grid, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
@@ -741,10 +802,8 @@ int launch_phase1_prefix_rows(const Phase1Geometry& g, const uint16_t* q_rot,
   a.n_rt = (int32_t)((n + g.rows_per_wg - 1) / g.rows_per_wg);
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.head_dim));
   const int grid = a.n_rt * g.n_kv_heads * g.n_head_sub;
-  if (g.head_dim == 128)
-    hipLaunchKernelGGL((phase1_kernel<128, true>), dim3(grid), dim3(NTHR), 0, stream, a);
-  else
-    hipLaunchKernelGGL((phase1_kernel<64, true>), dim3(grid), dim3(NTHR), 0, stream, a);
+  if (g.head_dim == 128) launch_p1<128, true>(g, grid, stream, a);
+  else launch_p1<64, true>(g, grid, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
