@@ -22,6 +22,7 @@ import collections
 import csv
 import json
 import os
+import re
 import sys
 
 KERNELS = ("phase1_kernel", "phase2_kernel", "phase2_prep", "rope_fill", "v_cache_fill",
@@ -32,10 +33,12 @@ COPY_MARK = "neg_kernel"
 
 def short_name(full: str) -> str:
     # the second template argument tells the forms of the attention kernels apart
-    if "phase1_kernel" in full and ", true>" in full:
-        return "phase1_kernel_prefix_rows"
-    if "phase2_kernel" in full and ", true>" in full:
-        return "phase2_kernel_decode"
+    # (prefix rows, decode); a third, the wave count, does not
+    m = re.search(r"phase([12])_kernel<\s*\d+\s*,\s*(true|false)\b", full)
+    if m:
+        if m.group(1) == "1":
+            return "phase1_kernel_prefix_rows" if m.group(2) == "true" else "phase1_kernel"
+        return "phase2_kernel_decode" if m.group(2) == "true" else "phase2_kernel"
     for k in KERNELS:
         if k in full:
             return k

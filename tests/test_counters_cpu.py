@@ -47,6 +47,9 @@ def test_template_forms_are_told_apart():
     assert counters.short_name("void pulsar::phase1_kernel<128, false>(pulsar::P1Args)") == "phase1_kernel"
     assert counters.short_name("void pulsar::phase1_kernel<128, true>(pulsar::P1Args)") == "phase1_kernel_prefix_rows"
     assert counters.short_name("void pulsar::phase2_kernel<64, true>(pulsar::P2Args)") == "phase2_kernel_decode"
+    # a third template argument (the wave count) keeps the form
+    assert counters.short_name("void pulsar::phase1_kernel<128, false, 12>(pulsar::P1Args)") == "phase1_kernel"
+    assert counters.short_name("void pulsar::phase1_kernel<64, true, 8>(pulsar::P1Args)") == "phase1_kernel_prefix_rows"
 
 
 def test_matrix_summary_per_dispatch_and_over_compute(tmp_path):
