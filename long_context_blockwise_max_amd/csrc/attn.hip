@@ -166,9 +166,11 @@ __device__ __forceinline__ void sub_qk(const char* stage, int kt, const bf16x8 (
   }
 }
 
-// sub_qk with the query rows staged in LDS (laid out like K tile rows).
-template <int D>
-__device__ __forceinline__ void sub_qk_lds(const char* stage, int kt, const char* qlds, f32x16& s) {
+// sub_qk with the query rows staged in LDS (laid out like K tile rows); the
+// first QR fragments come from registers.
+template <int D, int QR>
+__device__ __forceinline__ void sub_qk_lds(const char* stage, int kt, const char* qlds,
+                                           const bf16x8 (&q)[D / 16], f32x16& s) {
   using KTl = KTile<D>;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
@@ -178,7 +180,7 @@ __device__ __forceinline__ void sub_qk_lds(const char* stage, int kt, const char
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     const bf16x8 a = *(const bf16x8*)(stage + KTl::off(krow, 16 * ks + 8 * half));
-    const bf16x8 b = *(const bf16x8*)(qlds + KTl::off(lane & 31, 16 * ks + 8 * half));
+    const bf16x8 b = ks < QR ? q[ks] : *(const bf16x8*)(qlds + KTl::off(lane & 31, 16 * ks + 8 * half));
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s, 0, 0, 0);
   }
 }
@@ -438,9 +440,12 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(64 * NWV, 64 * NWV),
                                amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
 phase1_kernel(P1Args a) {
   constexpr int NQ = 1;
-  // With 12 waves (3 per SIMD) the registers no longer hold the query rows: they
-  // sit in LDS behind the two slots (8 KB per wave at d = 128, 160 KB in all).
+  // With 12 waves (3 per SIMD) the registers no longer hold all of the query
+  // rows: they sit in LDS behind the two slots (8 KB per wave at d = 128, 160 KB
+  // in all), and only the first QRN fragments are also kept in registers (as many
+  // as fit the 168-register budget at d = 128: half the LDS reads of Q go away).
   constexpr bool QL = NWV > NW;
+  constexpr int QRN = D / 32;
   constexpr int QBYTES = 32 * KTile<D>::ROWB;
   __shared__ __attribute__((aligned(1024))) char smem[2 * Stage<D>::BYTES + (QL ? NWV * QBYTES : 0)];
 
@@ -499,6 +504,16 @@ phase1_kernel(P1Args a) {
       }
       const int c = (lane % KTl::CPR) ^ KTl::sw(row);
       dma16(a.q + (pos * a.hq + h) * D + 8 * c, qlds + x * 1024);
+    }
+    if constexpr (QRN > 0) {   // the register-held fragments (load_q's others go unused)
+      const int r = r0 + lr;
+      int64_t pos = (int64_t)i * a.b + r;
+      if constexpr (PR) {
+        const int64_t kr = r < n_rows ? krow[r] : 0;
+        const int64_t hb = (int64_t)a.hkv * a.b;
+        pos = (kr / hb) * a.b + kr % hb;
+      }
+      load_q<D>(r < n_rows ? a.q + (pos * a.hq + h) * D : nullptr, qf[0]);
     }
   } else {
     const int r = r0 + lr;
@@ -621,7 +636,7 @@ phase1_kernel(P1Args a) {
       const bool act = __ballot(lim > 0) != 0;   // else past the list, or above the diagonal
       f32x16 s;
       if (act) {
-        if constexpr (QL) sub_qk_lds<D>(stg, kt, qlds, s);
+        if constexpr (QL) sub_qk_lds<D, QRN>(stg, kt, qlds, qf[0], s);
         else sub_qk<D>(stg, kt, qf[0], s);
       }
       if (more) stage(t + 1, nxt, kt);
