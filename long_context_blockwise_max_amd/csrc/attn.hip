@@ -442,10 +442,11 @@ phase1_kernel(P1Args a) {
   constexpr int NQ = 1;
   // With 12 waves (3 per SIMD) the registers no longer hold all of the query
   // rows: they sit in LDS behind the two slots (8 KB per wave at d = 128, 160 KB
-  // in all), and only the first QRN fragments are also kept in registers (as many
-  // as fit the 168-register budget at d = 128: half the LDS reads of Q go away).
+  // in all), and only the first QRN fragments are also kept in registers: 6 of 8
+  // fit the 168-register budget at d = 128 (its few spills fall outside the
+  // loop), all 4 at d = 64.
   constexpr bool QL = NWV > NW;
-  constexpr int QRN = D / 32;
+  constexpr int QRN = D == 128 ? 6 : D / 16;
   constexpr int QBYTES = 32 * KTile<D>::ROWB;
   __shared__ __attribute__((aligned(1024))) char smem[2 * Stage<D>::BYTES + (QL ? NWV * QBYTES : 0)];
 
