@@ -203,9 +203,14 @@ int pulsar_phase1_prefix_rows(const pulsar_geom* g, const pulsar_attn* a,
                               const uint16_t* k_cache, const uint16_t* v_cache, float* o_prefix,
                               void* ws, size_t ws_bytes, void* stream);
 
-/* Number of partial results pulsar_phase2_query writes per sequence for this
- * shape: every shard is split into the same number of contiguous key ranges,
- * plus one part for the self shard when has_self != 0.  Returns <= 0 on error. */
+/* Number of partial results pulsar_phase2_query and pulsar_phase2_decode write
+ * per sequence for this shape: the key tiles of every retained shard, in shard
+ * order, followed by the self shard's tiles, are cut into this many contiguous
+ * ranges of (almost) equal length, so a part may span two shards or a shard and
+ * the self shard.  It does not depend on has_self or on the self length, except
+ * that with no shard (n_shards = 0, has_self != 0) there is one part.  A part
+ * whose keys a query token may not see (the self shard is causal) holds LSE
+ * -inf and a zero output for that token.  Returns <= 0 on error. */
 int32_t pulsar_phase2_num_parts(const pulsar_attn* a, int32_t batch, int32_t n_shards,
                                 int32_t shard_len, int32_t q_len, int32_t has_self);
 
@@ -216,9 +221,10 @@ size_t pulsar_phase2_workspace_bytes(const pulsar_attn* a, int32_t batch, int32_
 
 /* Phase-2 query attention over retained shards ("Dropping the Anchor ..."
  * Section 2.2).  Query token t of sequence s sits at position q_pos0 + t.  For
- * every part (a contiguous key range of one shard, or the self shard) the call
- * writes the softmax-normalised partial output and its log-sum-exp (natural
- * log of sum exp(q.k / sqrt(d)) over the part's keys).  The self shard holds
+ * every part (a contiguous range of the shards' and the self shard's keys, as
+ * pulsar_phase2_num_parts describes) the call writes the softmax-normalised
+ * partial output and its log-sum-exp (natural log of sum exp(q.k / sqrt(d))
+ * over the part's keys that the token sees).  The self shard holds
  * the query tokens' own keys and values, attended causally (token t sees self
  * keys 0..t); pass k_self = v_self = NULL to attend to the retained shards only.
  *   qq               [B][Lq][Hq][d] bf16, pre-RoPE
@@ -262,8 +268,9 @@ int pulsar_self_append(const pulsar_attn* a, int32_t batch, int32_t cap, int32_t
  * generated token per step is q_len = 1).  Query token t is self token
  * n_self - q_len + t, at position self_pos0 + n_self - q_len + t; it attends to
  * every key of the retained shards and to self tokens 0 .. n_self - q_len + t.
- * Writes partials exactly as pulsar_phase2_query with a self shard (its last
- * part is the self cache), to be merged with pulsar_lse_merge.
+ * Writes partials exactly as pulsar_phase2_query with a self shard (the self
+ * cache's tiles follow the shards' in the parts), to be merged with
+ * pulsar_lse_merge.
  *   qq                 [B][q_len][Hq][d] bf16, pre-RoPE
  *   k_cache, v_cache   retained shards, as in pulsar_phase2_query
  *   k_self_cache, v_self_cache, cap   filled by pulsar_self_append, n_self tokens

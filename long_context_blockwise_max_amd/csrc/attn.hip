@@ -867,20 +867,9 @@ phase2_kernel(P2Args a) {
   constexpr int TAB = KSPLIT ? QTab<D>::BYTES : 0;
   __shared__ __attribute__((aligned(1024))) char smem[NSLOT * Stage<D>::BYTES + TAB];
 
-  // Workgroups take the shard parts first and the short self parts last, so
-  // that the long parts all start in the first waves of workgroups and finish
-  // together (interleaved self parts staggered them and left a tail).
   int w = blockIdx.x;
-  const int n_big = a.n_shards * a.splits;
-  const int total_big = a.batch * a.hkv * a.n_rg * n_big;
-  int p;
-  if (w < total_big) {
-    p = w % n_big;
-    w /= n_big;
-  } else {
-    p = n_big;
-    w -= total_big;
-  }
+  const int p = w % a.n_parts;
+  w /= a.n_parts;
   const int rg = w % a.n_rg;
   w /= a.n_rg;
   const int g = w % a.hkv;
@@ -895,32 +884,48 @@ phase2_kernel(P2Args a) {
   constexpr bool key_split = KSPLIT;
   const int row_base = key_split ? 0 : rg * (NW * 32) + wave * 32;
 
-  // key source of this part: a contiguous range of one retained shard, or the
-  // query tokens' own keys, attended causally
-  const bool self_part = p >= a.n_shards * a.splits;
-  int k0 = 0, k1 = 0;
-  const uint16_t* kbase;
-  const uint16_t* vbase;
-  int64_t k_ld, v_ld;
-  if (!self_part) {
-    const int shard = p / a.splits;
-    const int sp = p % a.splits;
-    const int nt = (a.n + KT - 1) / KT;
-    k0 = (int)(((int64_t)sp * nt) / a.splits) * KT;
-    k1 = min((int)(((int64_t)(sp + 1) * nt) / a.splits) * KT, a.n);
-    const int64_t base = (((int64_t)bb * a.n_shards + shard) * a.hkv + g) * a.n * D;
-    kbase = a.kc + base;
-    vbase = a.vc + base;
-    k_ld = D;
-    v_ld = a.n;
-  } else {
-    k1 = a.n_self;
-    kbase = a.ks + (int64_t)bb * a.ks_seq + (int64_t)g * D;
-    vbase = a.vs + (int64_t)bb * a.vs_seq + (int64_t)g * D * a.vs_ld;
-    k_ld = (int64_t)a.hkv * D;
-    v_ld = a.vs_ld;
-  }
-  const int n_tiles = (k1 - k0 + KT - 1) / KT;
+  // Key tiles of this (sequence, KV head): every retained shard's tiles in shard
+  // order, then the self tiles.  The parts take equal contiguous ranges of them,
+  // so the self keys add at most one tile to a part instead of a part of their own.
+  const int nt = (a.n + KT - 1) / KT;
+  const int64_t shard_tiles = (int64_t)a.n_shards * nt;
+  const int64_t all_tiles = shard_tiles + (a.n_self + KT - 1) / KT;
+  const int64_t t0 = (int64_t)p * all_tiles / a.n_parts;
+  const int n_tiles = (int)((int64_t)(p + 1) * all_tiles / a.n_parts - t0);
+  // Source of the part's tile u (past the part: its last tile, staged but never
+  // read): keys lo .. hi - 1 of one shard, or of the self shard, which is
+  // attended causally.
+  struct Src {
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t k_ld, v_ld;
+    int lo, hi;
+    bool causal;
+  };
+  auto tile_src = [&](int u) __attribute__((always_inline)) {
+    const int64_t gt = t0 + min(u, n_tiles - 1);
+    Src r;
+    if (gt < shard_tiles) {
+      const int shard = (int)(gt / nt);
+      const int64_t base = (((int64_t)bb * a.n_shards + shard) * a.hkv + g) * a.n * D;
+      r.k = a.kc + base;
+      r.v = a.vc + base;
+      r.k_ld = D;
+      r.v_ld = a.n;
+      r.lo = (int)(gt - (int64_t)shard * nt) * KT;
+      r.hi = a.n;
+      r.causal = false;
+    } else {
+      r.k = a.ks + (int64_t)bb * a.ks_seq + (int64_t)g * D;
+      r.v = a.vs + (int64_t)bb * a.vs_seq + (int64_t)g * D * a.vs_ld;
+      r.k_ld = (int64_t)a.hkv * D;
+      r.v_ld = a.vs_ld;
+      r.lo = (int)(gt - shard_tiles) * KT;
+      r.hi = a.n_self;
+      r.causal = true;
+    }
+    return r;
+  };
 
   // query fragments: row fr = head-in-group * Lq + token
   bf16x8 qf[NQ][D / 16];
@@ -938,20 +943,21 @@ phase2_kernel(P2Args a) {
   FlashState<D, NQ> st;
   flash_init(st);
 
-  // keys past the part read its first key (masked below)
-  auto src_of = [&](int t) __attribute__((always_inline)) {
+  // keys past the source read the tile's first key (masked below)
+  auto stage_part_tile = [&](char* dst, int u) __attribute__((always_inline)) {
+    const Src r = tile_src(u);
     TileSrc<D> sr;
 #pragma unroll
     for (int x = 0; x < KTile<D>::NI; ++x) {
-      const int kk = k0 + t * KT + staged_k_row<D>(x);
-      sr.k[x] = (int64_t)(kk < k1 ? kk : k0) * k_ld;
+      const int kk = r.lo + staged_k_row<D>(x);
+      sr.k[x] = (int64_t)(kk < r.hi ? kk : r.lo) * r.k_ld;
     }
 #pragma unroll
     for (int x = 0; x < VTile<D>::NI; ++x) {
-      const int kk = k0 + t * KT + 8 * staged_v_chunk<D>(x);
-      sr.v[x] = kk < k1 ? kk : k0;
+      const int kk = r.lo + 8 * staged_v_chunk<D>(x);
+      sr.v[x] = kk < r.hi ? kk : r.lo;
     }
-    return sr;
+    stage_tile<D>(dst, r.k, r.v, r.v_ld, sr);
   };
   // Every iteration issues the same ND loads per wave (tiles past the part are
   // staged into a free slot and never read), so at each barrier exactly the
@@ -970,7 +976,7 @@ phase2_kernel(P2Args a) {
     }
   }
 #pragma unroll
-  for (int u = 0; u < AHEAD; ++u) stage_tile<D>(slot(u), kbase, vbase, v_ld, src_of(u));
+  for (int u = 0; u < AHEAD; ++u) stage_part_tile(slot(u), u);
   if (rotate_q) {
     // Each lane turns the pairs (i, i + D/2) it holds: i = 16 ks + 8 half + j for
     // ks < D/32, the partner in fragment ks + D/32.
@@ -992,16 +998,17 @@ phase2_kernel(P2Args a) {
   const float sl2 = a.scale_log2;
   for (int t = 0; t < n_tiles; ++t) {
     tile_barrier_n<(AHEAD - 1) * ND>();   // tile t has landed; every wave is past its reads of tile t-1
-    stage_tile<D>(slot(t + AHEAD), kbase, vbase, v_ld, src_of(t + AHEAD));   // into the slot of tile t-1
+    stage_part_tile(slot(t + AHEAD), t + AHEAD);   // into the slot of tile t-1
     if (!wave_active) continue;
     const char* stg = slot(t);
+    const Src r = tile_src(t);
 #pragma unroll
     for (int kt = 0; kt < NSUB; ++kt) {
       if (key_split && kt != wave) continue;
-      // a shard part sees all its keys; the self part sees self tokens up to the
-      // query token itself (query token tok is self token n_self - Lq + tok)
-      const int kb = k0 + t * KT + kt * 32;
-      const int lim = self_part ? min(a.n_self - a.lq + tok - kb + 1, k1 - kb) : k1 - kb;
+      // shard keys are all visible; self keys up to the query token itself
+      // (query token tok is self token n_self - Lq + tok)
+      const int kb = r.lo + kt * 32;
+      const int lim = r.causal ? min(a.n_self - a.lq + tok - kb + 1, r.hi - kb) : r.hi - kb;
       if (!__ballot(lim > 0)) break;
       f32x16 s;
       bf16x8 p[2];
@@ -1079,7 +1086,8 @@ Phase2Geometry phase2_geometry(int32_t batch, int32_t n_shards, int32_t shard_le
   if (splits > nt) splits = nt;
   if (splits < 1) splits = 1;
   g.splits = (int32_t)splits;
-  g.n_parts = n_shards * g.splits + g.has_self;
+  // the self tiles join the shards' tiles; with no shard one part holds them
+  g.n_parts = n_shards > 0 ? n_shards * g.splits : 1;
   g.self_pad = (q_len + KT - 1) / KT * KT;
   return g;
 }

@@ -156,11 +156,12 @@ def test_phase1_halves_reject_bad_arguments():
 
 @needs_lib
 def test_phase2_part_count_and_rejections():
+    # every shard split alike; the self tiles share the shards' parts
     n = B.pulsar_phase2_num_parts(ATTN, 1, 8, 16384, 64, True)
-    assert n >= 9 and (n - 1) % 8 == 0
-    n0 = B.pulsar_phase2_num_parts(ATTN, 1, 8, 16384, 64, False)
-    assert n0 == n - 1
-    assert B.pulsar_phase2_num_parts(ATTN, 8, 16, 32768, 1, True) >= 17
+    assert n >= 8 and n % 8 == 0
+    assert B.pulsar_phase2_num_parts(ATTN, 1, 8, 16384, 64, False) == n
+    assert B.pulsar_phase2_num_parts(ATTN, 8, 16, 32768, 1, True) >= 16
+    assert B.pulsar_phase2_num_parts(ATTN, 2, 0, 0, 64, True) == 1     # the self shard only
     # tiny shards never get an empty part
     for shard_len in (1, 63, 64, 65, 200):
         nn = B.pulsar_phase2_num_parts(ATTN, 1, 2, shard_len, 4, False)

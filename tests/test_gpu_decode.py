@@ -41,6 +41,9 @@ CASES = {
 # so the zero-padded tail of the value runs moves several times)
 N_GEN = {"long_gen": 22}
 CASES["long_gen"] = dict(n_blocks=2, block_size=256, q_len=3, batch=2, n_planted=0)
+# a self cache of 201-203 tokens (4 tiles) next to 4 shard tiles: half the parts
+# read self keys only
+CASES["self_heavy"] = dict(n_blocks=2, block_size=128, budget_chunks=1, q_len=200, n_planted=0)
 
 
 @pytest.mark.parametrize("name", list(CASES))

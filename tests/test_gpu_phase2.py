@@ -59,6 +59,11 @@ SMALL = {
                     budget_chunks=1, n_planted=0),
     "no_sink_batch2": dict(n_blocks=3, block_size=256, sink_size=0, budget_chunks=2, q_len=7,
                            batch=2, n_planted=0),
+    # more self tiles (5) than shard tiles (4): the parts past the shards hold self
+    # tiles only, and the last one holds keys that the early query tokens must not
+    # see (those rows give an empty part, LSE -inf)
+    "self_spans_parts": dict(n_blocks=2, block_size=128, budget_chunks=1, q_len=300,
+                             n_planted=0),
 }
 
 
