@@ -892,9 +892,8 @@ phase2_kernel(P2Args a) {
   const int64_t all_tiles = shard_tiles + (a.n_self + KT - 1) / KT;
   const int64_t t0 = (int64_t)p * all_tiles / a.n_parts;
   const int n_tiles = (int)((int64_t)(p + 1) * all_tiles / a.n_parts - t0);
-  // Source of the part's tile u (past the part: its last tile, staged but never
-  // read): keys lo .. hi - 1 of one shard, or of the self shard, which is
-  // attended causally.
+  // Source of a tile: keys lo .. hi - 1 of one shard, or of the self shard, which
+  // is attended causally.
   struct Src {
     const uint16_t* k;
     const uint16_t* v;
@@ -902,17 +901,35 @@ phase2_kernel(P2Args a) {
     int lo, hi;
     bool causal;
   };
-  auto tile_src = [&](int u) __attribute__((always_inline)) {
-    const int64_t gt = t0 + min(u, n_tiles - 1);
+  // Tile cursor: tile lt of shard `shard`, shard n_shards being the self shard.
+  // Staging and compute each walk the part's tiles with one, so no tile index is
+  // divided inside the loop.
+  struct Cur {
+    int shard, lt;
+  };
+  Cur first;
+  if (t0 < shard_tiles) {
+    first.shard = (int)(t0 / nt);
+    first.lt = (int)(t0 - (int64_t)first.shard * nt);
+  } else {
+    first.shard = a.n_shards;
+    first.lt = (int)(t0 - shard_tiles);
+  }
+  auto advance = [&](Cur& c) __attribute__((always_inline)) {
+    if (++c.lt == nt && c.shard < a.n_shards) {
+      c.lt = 0;
+      ++c.shard;
+    }
+  };
+  auto src_of = [&](const Cur& c) __attribute__((always_inline)) {
     Src r;
-    if (gt < shard_tiles) {
-      const int shard = (int)(gt / nt);
-      const int64_t base = (((int64_t)bb * a.n_shards + shard) * a.hkv + g) * a.n * D;
+    r.lo = c.lt * KT;
+    if (c.shard < a.n_shards) {
+      const int64_t base = (((int64_t)bb * a.n_shards + c.shard) * a.hkv + g) * a.n * D;
       r.k = a.kc + base;
       r.v = a.vc + base;
       r.k_ld = D;
       r.v_ld = a.n;
-      r.lo = (int)(gt - (int64_t)shard * nt) * KT;
       r.hi = a.n;
       r.causal = false;
     } else {
@@ -920,7 +937,6 @@ phase2_kernel(P2Args a) {
       r.v = a.vs + (int64_t)bb * a.vs_seq + (int64_t)g * D * a.vs_ld;
       r.k_ld = (int64_t)a.hkv * D;
       r.v_ld = a.vs_ld;
-      r.lo = (int)(gt - shard_tiles) * KT;
       r.hi = a.n_self;
       r.causal = true;
     }
@@ -944,8 +960,8 @@ phase2_kernel(P2Args a) {
   flash_init(st);
 
   // keys past the source read the tile's first key (masked below)
-  auto stage_part_tile = [&](char* dst, int u) __attribute__((always_inline)) {
-    const Src r = tile_src(u);
+  auto stage_part_tile = [&](char* dst, const Cur& c) __attribute__((always_inline)) {
+    const Src r = src_of(c);
     TileSrc<D> sr;
 #pragma unroll
     for (int x = 0; x < KTile<D>::NI; ++x) {
@@ -975,8 +991,14 @@ phase2_kernel(P2Args a) {
       tab[e] = make_float2(c, sn);
     }
   }
+  // tiles past the part: the staging cursor stays on the last tile (staged into a
+  // free slot, never read)
+  Cur sc = first;
 #pragma unroll
-  for (int u = 0; u < AHEAD; ++u) stage_part_tile(slot(u), u);
+  for (int u = 0; u < AHEAD; ++u) {
+    stage_part_tile(slot(u), sc);
+    if (u < n_tiles - 1) advance(sc);
+  }
   if (rotate_q) {
     // Each lane turns the pairs (i, i + D/2) it holds: i = 16 ks + 8 half + j for
     // ks < D/32, the partner in fragment ks + D/32.
@@ -996,12 +1018,15 @@ phase2_kernel(P2Args a) {
     }
   }
   const float sl2 = a.scale_log2;
+  Cur cc = first;
   for (int t = 0; t < n_tiles; ++t) {
     tile_barrier_n<(AHEAD - 1) * ND>();   // tile t has landed; every wave is past its reads of tile t-1
-    stage_part_tile(slot(t + AHEAD), t + AHEAD);   // into the slot of tile t-1
+    stage_part_tile(slot(t + AHEAD), sc);   // into the slot of tile t-1
+    if (t + AHEAD < n_tiles - 1) advance(sc);
     if (!wave_active) continue;
     const char* stg = slot(t);
-    const Src r = tile_src(t);
+    const Src r = src_of(cc);
+    advance(cc);
 #pragma unroll
     for (int kt = 0; kt < NSUB; ++kt) {
       if (key_split && kt != wave) continue;
