@@ -133,3 +133,35 @@ def test_merge_of_only_empty_parts_is_zero_with_lse_minus_inf():
     torch.cuda.synchronize()
     assert torch.all(o == 0).item()
     assert torch.all(lse == float("-inf")).item()
+
+
+@pytest.mark.parametrize("hq,hkv,d,lq", [(4, 2, 64, 150), (8, 2, 128, 70), (4, 2, 64, 1)])
+def test_query_over_the_self_shard_only(hq, hkv, d, lq):
+    """No retained shard (n_shards = 0): one part, the causal self shard, spread
+    over several tiles for the longer queries (the last case is the decode form)."""
+    torch = torch_cuda()
+    from long_context_blockwise_max_amd import binding as B
+    w = W.with_(W.WORKLOADS["tiny"], name="self_only", n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                q_len=lq, batch=2)
+    qq, kq, vq = W.query(w)
+    attn = B.make_attn(hq, hkv, d, w.rope_base, 0)
+    n_parts = B.pulsar_phase2_num_parts(attn, w.batch, 0, 0, lq, True)
+    assert n_parts == 1
+    dev = torch.device("cuda")
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    o_part = torch.full((w.batch, 1, lq, hq, d), float("nan"), device=dev)
+    lse_part = torch.full((w.batch, 1, lq, hq), float("nan"), device=dev)
+    ws = torch.empty(B.pulsar_phase2_workspace_bytes(attn, w.batch, lq, True), dtype=torch.uint8,
+                     device=dev)
+    log(f"[self-only] hq={hq} hkv={hkv} d={d} lq={lq}")
+    B.pulsar_phase2_query(attn, w.batch, 0, 0, bf(qq), lq, w.context_len, None, None, bf(kq), bf(vq),
+                          o_part, lse_part, n_parts, ws)
+    torch.cuda.synchronize()
+    o, lse = o_part.cpu().numpy(), lse_part.cpu().numpy()
+    empty = np.zeros((0, hkv, 8, d))
+    for s in range(w.batch):
+        (want_o, want_lse), = OA.phase2_partials(W.bf16_bits_to_f64(qq[s]), w.context_len, empty, empty,
+                                                 W.bf16_bits_to_f64(kq[s]), W.bf16_bits_to_f64(vq[s]),
+                                                 w.rope_base)
+        assert_close(o[s, 0], want_o, f"self-only O seq {s}")
+        assert_close(lse[s, 0], want_lse, f"self-only LSE seq {s}", max_abs=LSE_ABS, mean_abs=LSE_ABS)
