@@ -25,8 +25,8 @@
 // Phase 1, global_load_lds_dwordx4 in Phase 2), one barrier per tile: two slots,
 // one tile ahead, for Phase 1 and the Phase-2 query; four slots, three tiles
 // ahead, for the Phase-2 decode form, which streams from HBM with little work
-// per tile.  The 16-byte chunks of every LDS
-// row are XOR-swizzled so that fragment reads are bank-conflict free.
+// per tile.  The 16-byte chunks of every LDS row are XOR-swizzled so that
+// fragment reads are bank-conflict free.
 //
 // Softmax runs in base 2: t = (q.k) * log2(e) / sqrt(d), p = exp2(t - m), with
 // the reference maximum m raised lazily (see kRescaleSlack).  P is rounded to
