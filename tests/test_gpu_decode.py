@@ -44,6 +44,8 @@ CASES["long_gen"] = dict(n_blocks=2, block_size=256, q_len=3, batch=2, n_planted
 # a self cache of 201-203 tokens (4 tiles) next to 4 shard tiles: half the parts
 # read self keys only
 CASES["self_heavy"] = dict(n_blocks=2, block_size=128, budget_chunks=1, q_len=200, n_planted=0)
+CASES["self_heavy_d128"] = dict(n_blocks=2, block_size=128, budget_chunks=1, q_len=200, n_planted=0,
+                                n_q_heads=8, n_kv_heads=2, head_dim=128, batch=2)
 
 
 @pytest.mark.parametrize("name", list(CASES))
