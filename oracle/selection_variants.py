@@ -27,11 +27,12 @@ query-free selection does not have.
 As for Max-IDF, ties go to the earlier chunk and the kept chunks are returned in
 ascending order; with k >= n_chunks every chunk is kept.
 
-Parity unpinned: the exact output sequence of `splitmix64`.  Its pins fix what
-the uniform method needs (every chunk kept with probability k / C, seeds that
-repeat and differ, balanced and uncorrelated bits), but a change to its
-finaliser that leaves it a good generator would pass them; the GPU side
-implements the same published definition.
+The exact output sequence of `splitmix64` is pinned by the generator's
+published known-answer values (the first outputs from one seed and the float
+bucket counts of 100,000 outputs from another, as the Rosetta Code task
+"Pseudo-random numbers/Splitmix64" states them); the statistical pins fix what
+the uniform method needs from it (every chunk kept with probability k / C,
+seeds that repeat and differ, balanced and uncorrelated bits).
 
 Exact ranking: mean_idf = ln N - (1/C) ln prod_pos df(t_pos), and
 H = ln C - (1/C) ln prod_v c_v^c_v = ln C - (1/C) ln prod_pos c(t_pos), where

@@ -303,6 +303,7 @@ VARIANT_PINS = [(TV.test_mean_idf_exact_order_equals_the_float_definition, (0,))
                 (TV.test_entropy_exact_order_equals_scipy_entropy, (4,)),
                 TV.test_entropy_closed_forms,
                 TV.test_uniform_selection_is_uniform_and_seeded,
+                TV.test_splitmix64_known_answers,
                 TV.test_even_spacing_closed_form]
 
 
@@ -348,6 +349,25 @@ def test_uniform_keys_without_the_block_in_the_counter_is_caught(monkeypatch):
         # every block draws the same counters
         return [[SV.splitmix64(seed, c + 1) for c in range(n_chunks)] for _ in range(n_blocks)]
     _caught_variant(monkeypatch, SV.uniform_keys, bad)
+
+
+def test_splitmix64_with_a_wrong_finaliser_shift_is_caught(monkeypatch):
+    def bad(seed, n):
+        # still a good generator (balanced, uncorrelated bits): only the last
+        # xor-shift of the finaliser differs from the published one
+        z = (seed + n * SV.GOLDEN_GAMMA) & SV.MASK64
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & SV.MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & SV.MASK64
+        return z ^ (z >> 29)
+    _caught_variant(monkeypatch, SV.splitmix64, bad)
+
+
+def test_splitmix64_counting_from_zero_is_caught(monkeypatch):
+    orig = SV.splitmix64
+
+    def bad(seed, n):
+        return orig(seed, n - 1)       # the state read before its first advance
+    _caught_variant(monkeypatch, SV.splitmix64, bad)
 
 
 def test_even_spacing_off_by_half_is_caught(monkeypatch):

@@ -127,6 +127,21 @@ def test_uniform_selection_is_uniform_and_seeded():
     assert a[0].tolist() != a[1].tolist() or k == C  # blocks draw different counters
 
 
+def test_splitmix64_known_answers():
+    """The published known-answer values of SplitMix64 (tests/golden/splitmix64_kat.json):
+    the first five outputs from one seed, and the float bucket counts of 100,000
+    outputs from another.  A wrong constant, shift or increment changes both."""
+    with open(os.path.join(GOLDEN, "splitmix64_kat.json")) as f:
+        kat = json.load(f)
+    got = [V.splitmix64(kat["seed"], n) for n in range(1, 6)]
+    assert got == [int(x) for x in kat["first_outputs"]]
+    nb = kat["histogram_buckets"]
+    counts = [0] * nb
+    for n in range(1, kat["histogram_n"] + 1):
+        counts[int(V.splitmix64(kat["histogram_seed"], n) / 2.0 ** 64 * nb)] += 1
+    assert counts == kat["histogram_counts"]
+
+
 def test_splitmix64_outputs_are_balanced():
     bits = np.array([[(V.splitmix64(99, n) >> i) & 1 for i in range(64)] for n in range(1, 4001)])
     frac = bits.mean(axis=0)
