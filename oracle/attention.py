@@ -82,6 +82,39 @@ def phase1_rows(q, k_hat, v, prefixes, rows, block_size, base):
     return np.stack(outs)
 
 
+def phase1_rows_in_block(q, k_hat, v, prefix_i, i, rows, block_size, base):
+    """Phase-1 output of several rows of one block: the definition of
+    phase1_rows (row r sees every entry of prefix_i, then the block's own rows
+    0..r), written as one masked softmax per head over the explicit key list
+    [prefix_i || own rows 0..max(rows)], own row j hidden from row r when j > r.
+
+    q, k_hat, v : indexable [L][H][d] as for phase1_rows
+    rows        : row indices within block i
+    returns O [len(rows)][Hq][d] float64
+    """
+    rows = np.asarray(rows, np.int64)
+    lo = i * block_size
+    r_max = int(rows.max())
+    prefix_i = np.asarray(prefix_i, np.int64)
+    keys = np.concatenate([prefix_i, np.arange(lo, lo + r_max + 1, dtype=np.int64)])
+    kh = np.asarray(k_hat[keys], np.float64)
+    vv = np.asarray(v[keys], np.float64)
+    pos = lo + rows
+    q_hat = rotate_bf16(np.asarray(q[pos], np.float64), pos, base)
+    hq, d = q_hat.shape[1], q_hat.shape[2]
+    group = hq // kh.shape[1]
+    visible = np.ones((len(rows), len(keys)), bool)
+    visible[:, len(prefix_i):] = np.arange(r_max + 1)[None, :] <= rows[:, None]
+    out = np.empty((len(rows), hq, d))
+    for h in range(hq):
+        g = h // group
+        s = np.where(visible, q_hat[:, h, :] @ kh[:, g, :].T / np.sqrt(d), -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        w = np.exp(s - m)
+        out[:, h, :] = (w @ vv[:, g, :]) / w.sum(axis=1, keepdims=True)
+    return out
+
+
 def phase1_block_dense(q, k_hat, v, prefix_i, i, block_size, base):
     """Twin formulation of Phase 1 for all rows of block i: one softmax over the
     whole preceding context with an additive bias, ln(multiplicity of the

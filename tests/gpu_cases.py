@@ -90,19 +90,24 @@ class Case:
         return out
 
 
-def sample_rows(w: W.Workload, per_block_random=3, seed=0, sparse=False):
-    """(block, row) pairs: the first and last rows, tile edges and a few seeded rows."""
+def dense_rows(w: W.Workload, blocks=None, span=96, edge=64, seed=0):
+    """(block, row) pairs of the dense full-size sample: in each chosen block the
+    first and last `edge` rows plus one seeded row in every `span`-row stretch
+    (so every 96- or 128-row tile of the block has at least one); the other
+    blocks get their first rows, the edges of their first 64-row tile, their
+    last row and two seeded rows."""
     rng = np.random.default_rng(seed)
     b = w.block_size
-    if sparse:
-        fixed = sorted({0, 63, 64, b - 1})
-    else:
-        fixed = sorted({0, 1, 31, 32, 63, 64, 127, 128, b // 2, b - 65, b - 64, b - 2, b - 1})
-    fixed = [r for r in fixed if 0 <= r < b]
+    blocks = range(w.n_blocks) if blocks is None else blocks
     rows = []
     for i in range(w.n_blocks):
-        rr = set(fixed) | set(int(x) for x in rng.integers(0, b, per_block_random))
-        rows += [(i, r) for r in sorted(rr)]
+        if i in blocks:
+            rr = set(range(min(edge, b))) | set(range(max(0, b - edge), b))
+            for lo in range(0, b, span):
+                rr.add(int(rng.integers(lo, min(lo + span, b))))
+        else:
+            rr = {0, 63, 64, b - 1} | set(int(x) for x in rng.integers(0, b, 2))
+        rows += [(i, r) for r in sorted(x for x in rr if 0 <= x < b)]
     return rows
 
 

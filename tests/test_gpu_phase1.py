@@ -10,7 +10,8 @@ import pytest
 import workloads as W
 from oracle import attention as OA
 from oracle import selection as OS
-from tests.gpu_cases import (Case, F32Rows, assert_close, log, sample_rows, torch_cuda)
+from tests.gpu_cases import (Case, F32Rows, assert_close, dense_rows, log, rope_spec,
+                              torch_cuda)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +52,8 @@ def _full_compare(case):
 
 
 def _sampled_compare(case, rows):
+    """Sampled rows against the oracle, all heads, one block at a time (the rows
+    of a block share their key list, so the oracle takes them together)."""
     import torch
     w = case.w
     sel, _, _ = case.oracle_selection()
@@ -58,11 +61,16 @@ def _sampled_compare(case, rows):
     np.testing.assert_array_equal(got_sel, sel)
     pre = OS.prefix_positions(sel, w.n_blocks, w.block_size, w.chunk_size, w.sink_size)
     khat = case.oracle_khat()
-    pos = torch.tensor([i * w.block_size + r for i, r in rows], device="cuda")
-    got = case.path.o.index_select(0, pos).cpu().numpy()
-    want = OA.phase1_rows(F32Rows(case.q), khat, F32Rows(case.v), pre, rows, w.block_size,
-                          w.rope_base)
-    assert_close(got, want, f"{w.name} phase1 sampled rows ({len(rows)} rows x {w.n_q_heads} heads)")
+    q, v = F32Rows(case.q), F32Rows(case.v)
+    got_all, want_all = [], []
+    for i in sorted({i for i, _ in rows}):
+        rr = [r for (j, r) in rows if j == i]
+        pos = torch.tensor([i * w.block_size + r for r in rr], device="cuda")
+        got_all.append(case.path.o.index_select(0, pos).cpu().numpy())
+        want_all.append(OA.phase1_rows_in_block(q, khat, v, pre[i], i, rr, w.block_size,
+                                                rope_spec(w)))
+    assert_close(np.concatenate(got_all), np.concatenate(want_all),
+                 f"{w.name} phase1 sampled rows ({len(rows)} rows x {w.n_q_heads} heads)")
 
 
 SMALL = {
@@ -116,13 +124,18 @@ def test_phase1_is_deterministic():
     assert torch.equal(a, case.path.o)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["32k", "128k", "128k_star", "512k"])
 def test_phase1_full_size_sampled(name):
+    """Full-size workloads in the benchmark's launch configuration: the first and
+    last 64 rows of a block plus one seeded row in every 96 rows (every row tile),
+    all heads, on every block (512K: on the first, a middle and the last block,
+    and a sparse sample of the others)."""
     w = W.WORKLOADS[name]
     case = Case(w, extra_seqs=False)
     case.run()
-    rows = sample_rows(w, per_block_random=1 if w.n_blocks > 8 else 3, seed=w.seed,
-                       sparse=w.n_blocks > 8)
+    blocks = None if w.n_blocks <= 8 else [0, w.n_blocks // 2, w.n_blocks - 1]
+    rows = dense_rows(w, blocks=blocks, seed=w.seed)
     _sampled_compare(case, rows)
 
 

@@ -102,6 +102,62 @@ def test_gather_form_equals_dense_form_with_multiplicity_bias():
         np.testing.assert_allclose(rows, dense, rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (8, 2)])
+def test_rows_in_block_single_block_is_plain_causal_attention(hq, hkv):
+    """The several-rows form on one block (no prefix) against torch's causal
+    scaled_dot_product_attention in float64, on a subset of the rows."""
+    b, d, base = 48, 32, 500000.0
+    q, k, v = _bf(_rand((b, hq, d), 11)), _bf(_rand((b, hkv, d), 12)), _bf(_rand((b, hkv, d), 13))
+    pos = np.arange(b)
+    k_hat = A.rotate_bf16(k, pos, base)
+    rows = [0, 1, 5, 31, 32, 47]
+    got = A.phase1_rows_in_block(q, k_hat, v, np.zeros(0, np.int64), 0, rows, b, base)
+    qh = torch.from_numpy(A.rotate_bf16(q, pos, base)).permute(1, 0, 2)[None]
+    kh = torch.from_numpy(k_hat).permute(1, 0, 2)[None]
+    vh = torch.from_numpy(v).permute(1, 0, 2)[None]
+    want = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, is_causal=True,
+                                                            enable_gqa=(hq != hkv))
+    want = want[0].permute(1, 0, 2).numpy()[rows]
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+def test_rows_in_block_equals_dense_form_with_multiplicity_bias():
+    """Row subsets (unsorted, repeated, ending below the block's end) of every
+    block against the dense twin, with a kept chunk inside the sink."""
+    N, b, chunk, sink, hq, hkv, d, base = 3, 64, 16, 32, 4, 2, 16, 500000.0
+    L = N * b
+    q, k, v = _bf(_rand((L, hq, d), 14)), _bf(_rand((L, hkv, d), 15)), _bf(_rand((L, hkv, d), 16))
+    sel = np.array([[0, 2], [1, 3], [0, 1]])
+    pre = S.prefix_positions(sel, N, b, chunk, sink)
+    k_hat = A.rotate_bf16(k, np.arange(L), base)
+    for i in range(N):
+        dense = A.phase1_block_dense(q, k_hat, v, pre[i], i, b, base)
+        for rows in ([0], [b - 1, 3, 17, 3], list(range(b)), [5, 40, 41]):
+            got = A.phase1_rows_in_block(q, k_hat, v, pre[i], i, rows, b, base)
+            np.testing.assert_allclose(got, dense[rows], rtol=1e-10, atol=1e-12)
+
+
+def test_rows_in_block_zero_keys_average_exactly_the_visible_values():
+    """K = 0: each output is the mean of the visible value rows (duplicates
+    counted), so position-coded values reveal the visible set."""
+    N, b, chunk, sink, d, base = 3, 64, 16, 32, 8, 500000.0
+    L = N * b
+    q = _bf(_rand((L, 2, d), 17))
+    k = np.zeros((L, 1, d))
+    v = np.zeros((L, 1, d))
+    v[:, 0, 0] = np.arange(L)
+    v[:, 0, 1] = np.arange(L) ** 2
+    sel = np.array([[0, 2], [1, 3], [0, 1]])
+    pre = S.prefix_positions(sel, N, b, chunk, sink)
+    for i in range(N):
+        rows = [0, 1, 17, b - 1]
+        got = A.phase1_rows_in_block(q, k, v, pre[i], i, rows, b, base)
+        for n, r in enumerate(rows):
+            vis = np.concatenate([np.asarray(pre[i], np.int64), np.arange(i * b, i * b + r + 1)])
+            np.testing.assert_allclose(got[n, :, 0], vis.mean(), rtol=1e-12)
+            np.testing.assert_allclose(got[n, :, 1], (vis.astype(float) ** 2).mean(), rtol=1e-12)
+
+
 def test_zero_keys_give_uniform_weights_over_the_visible_set():
     """K = 0 makes every score 0, so each output is the plain mean of the
     visible V rows, counting duplicates; with V encoding the position, the

@@ -63,6 +63,9 @@ PHASE1_PINS = [(TA.test_single_block_phase1_is_plain_causal_attention, (4, 2)),
                (TA.test_single_block_phase1_is_plain_causal_attention, (8, 2)),
                TA.test_gather_form_equals_dense_form_with_multiplicity_bias,
                TA.test_zero_keys_give_uniform_weights_over_the_visible_set]
+ROWS_IN_BLOCK_PINS = [(TA.test_rows_in_block_single_block_is_plain_causal_attention, (4, 2)),
+                      TA.test_rows_in_block_equals_dense_form_with_multiplicity_bias,
+                      TA.test_rows_in_block_zero_keys_average_exactly_the_visible_values]
 PHASE2_PINS = [(TA.test_lse_merge_of_shards_equals_dense_attention, (True,)),
                (TA.test_lse_merge_of_shards_equals_dense_attention, (False,)),
                TA.test_merge_is_independent_of_shard_order_and_split_points,
@@ -290,6 +293,39 @@ def test_prefix_row_without_itself_is_caught(monkeypatch):
     _caught(monkeypatch, A.prefix_rows, bad,
             [TA.test_prefix_rows_of_a_contiguous_prefix_are_textbook_causal_attention,
              TA.test_prefix_rows_gather_equals_multiplicity_bias_dense])
+
+
+def _rows_in_block_variant(strict_mask=False, drop_prefix=False, kv_mod=False):
+    def bad(q, k_hat, v, prefix_i, i, rows, block_size, base):
+        rows = np.asarray(rows, np.int64)
+        lo = i * block_size
+        r_max = int(rows.max())
+        prefix_i = np.asarray(prefix_i, np.int64)[:0 if drop_prefix else None]
+        keys = np.concatenate([prefix_i, np.arange(lo, lo + r_max + 1, dtype=np.int64)])
+        kh = np.asarray(k_hat[keys], np.float64)
+        vv = np.asarray(v[keys], np.float64)
+        pos = lo + rows
+        q_hat = A.rotate_bf16(np.asarray(q[pos], np.float64), pos, base)
+        hq, d = q_hat.shape[1], q_hat.shape[2]
+        hkv = kh.shape[1]
+        own = np.arange(r_max + 1)[None, :]
+        vis = np.ones((len(rows), len(keys)), bool)
+        vis[:, len(prefix_i):] = (own < rows[:, None]) if strict_mask else (own <= rows[:, None])
+        vis[:, len(prefix_i)] |= strict_mask       # keep every row non-empty
+        out = np.empty((len(rows), hq, d))
+        for h in range(hq):
+            g = h % hkv if kv_mod else h // (hq // hkv)
+            sc = np.where(vis, q_hat[:, h, :] @ kh[:, g, :].T / np.sqrt(d), -np.inf)
+            w = np.exp(sc - sc.max(axis=1, keepdims=True))
+            out[:, h, :] = (w @ vv[:, g, :]) / w.sum(axis=1, keepdims=True)
+        return out
+    return bad
+
+
+@pytest.mark.parametrize("kind", ["strict_mask", "drop_prefix", "kv_mod"])
+def test_rows_in_block_mistakes_are_caught(monkeypatch, kind):
+    _caught(monkeypatch, A.phase1_rows_in_block, _rows_in_block_variant(**{kind: True}),
+            ROWS_IN_BLOCK_PINS)
 
 
 # ------------------------------------------------------ selection methods
