@@ -244,6 +244,30 @@ int pulsar_phase2_query(const pulsar_attn* a, int32_t batch, int32_t n_shards,
                         float* lse_part, int32_t n_parts, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* pulsar_phase2_query for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops and harnesses that forbid allocation.
+ * Same arguments, results and errors as pulsar_phase2_query, without ws and
+ * ws_bytes: the workspace (rotated query, rotated self keys, d-major self values)
+ * lives in a fixed device array inside the library, one per device, held until
+ * the process ends.  The call allocates and frees nothing.
+ *  - Limit: pulsar_phase2_workspace_bytes(a, batch, q_len, has_self) must not
+ *    exceed pulsar_phase2_noalloc_max_bytes() (8 MiB: e.g. up to 678 query
+ *    tokens with their self shard at 32 query / 8 KV heads, d = 128); larger
+ *    requests return PULSAR_EUNSUPPORTED before anything is enqueued.
+ *  - The first call on a device (that device current) looks up the array's
+ *    device address; PULSAR_EHIP if that fails.
+ *  - Every call on one device uses the same array, which keeps the last call's
+ *    contents (nothing in it needs clearing: each call writes what it reads).
+ *    Calls that overlap on one device -- on different streams, or from several
+ *    threads without ordering -- race; order them on one stream. */
+int pulsar_phase2_query_noalloc(const pulsar_attn* a, int32_t batch, int32_t n_shards,
+                                int32_t shard_len, const uint16_t* qq, int32_t q_len,
+                                int64_t q_pos0, const uint16_t* k_cache, const uint16_t* v_cache,
+                                const uint16_t* k_self, const uint16_t* v_self, float* o_part,
+                                float* lse_part, int32_t n_parts, void* stream);
+/* Size in bytes of the fixed array behind pulsar_phase2_query_noalloc. */
+size_t pulsar_phase2_noalloc_max_bytes(void);
+
 /* Generation ("Dropping the Anchor ..." Section 2.2, with the generated tokens
  * of Section 5's --tokens_to_generate): the query host keeps its own tokens --
  * the query, then every generated token -- in a self cache, and each new token

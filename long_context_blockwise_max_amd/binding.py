@@ -26,6 +26,7 @@ EXPORTED = (
     "pulsar_phase1_prepare", "pulsar_phase1_attend", "pulsar_self_append", "pulsar_phase2_decode",
     "pulsar_prefix_rows_len", "pulsar_phase1_prefix_rows",
     "pulsar_phase2_num_parts", "pulsar_phase2_workspace_bytes", "pulsar_phase2_query",
+    "pulsar_phase2_query_noalloc", "pulsar_phase2_noalloc_max_bytes",
     "pulsar_lse_merge", "pulsar_strerror",
 )
 
@@ -81,6 +82,11 @@ def lib():
         L.pulsar_phase2_query.argtypes = [A, i32, i32, i32, vp, i32, i64, vp, vp, vp, vp, vp, vp,
                                           i32, vp, sz, vp]
         L.pulsar_phase2_query.restype = ctypes.c_int
+        L.pulsar_phase2_query_noalloc.argtypes = [A, i32, i32, i32, vp, i32, i64, vp, vp, vp, vp,
+                                                  vp, vp, i32, vp]
+        L.pulsar_phase2_query_noalloc.restype = ctypes.c_int
+        L.pulsar_phase2_noalloc_max_bytes.argtypes = []
+        L.pulsar_phase2_noalloc_max_bytes.restype = sz
         L.pulsar_prefix_rows_len.argtypes = [G]
         L.pulsar_prefix_rows_len.restype = i64
         L.pulsar_phase1_prefix_rows.argtypes = [G, A, vp, vp, vp, vp, sz, vp]
@@ -263,6 +269,30 @@ def pulsar_phase2_query(attn: Attn, batch, n_shards, shard_len, qq, q_len, q_pos
         _ptr(o_part, torch.float32, rows * d, "o_part"), _ptr(lse_part, torch.float32, rows, "lse_part"),
         n_parts, _ptr(ws, torch.uint8, 0, "ws"), ws.numel(), _stream(stream))
     _check(rc, "pulsar_phase2_query")
+
+
+def pulsar_phase2_query_noalloc(attn: Attn, batch, n_shards, shard_len, qq, q_len, q_pos0,
+                                k_cache, v_cache, k_self, v_self, o_part, lse_part, n_parts,
+                                stream=None):
+    """pulsar_phase2_query with the library's fixed scratch in place of a workspace."""
+    import torch
+    hq, hkv, d = attn.n_q_heads, attn.n_kv_heads, attn.head_dim
+    kv_n = batch * n_shards * hkv * shard_len * d
+    self_n = batch * q_len * hkv * d
+    rows = batch * n_parts * q_len * hq
+    rc = lib().pulsar_phase2_query_noalloc(
+        ctypes.byref(attn), batch, n_shards, shard_len, _bf16(qq, batch * q_len * hq * d, "qq"),
+        q_len, int(q_pos0), _bf16(k_cache, kv_n, "k_cache", allow_none=n_shards == 0),
+        _bf16(v_cache, kv_n, "v_cache", allow_none=n_shards == 0),
+        _bf16(k_self, self_n, "k_self", allow_none=True),
+        _bf16(v_self, self_n, "v_self", allow_none=True),
+        _ptr(o_part, torch.float32, rows * d, "o_part"), _ptr(lse_part, torch.float32, rows, "lse_part"),
+        n_parts, _stream(stream))
+    _check(rc, "pulsar_phase2_query_noalloc")
+
+
+def pulsar_phase2_noalloc_max_bytes() -> int:
+    return lib().pulsar_phase2_noalloc_max_bytes()
 
 
 def pulsar_prefix_rows_len(geom: Geom) -> int:

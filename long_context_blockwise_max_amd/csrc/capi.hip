@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/pulsar.h"
 #include "launch.hpp"
 
@@ -249,6 +251,85 @@ int prepare_pointers_ok(const pulsar_geom* g, const uint16_t* q, const uint16_t*
   return PULSAR_OK;
 }
 
+// Checks shared by the two Phase-2 query calls (everything but the workspace);
+// fills the launch geometry.
+int phase2_query_checked(const pulsar_attn* a, int32_t batch, int32_t n_shards,
+                         int32_t shard_len, const uint16_t* qq, int32_t q_len, int64_t q_pos0,
+                         const uint16_t* k_cache, const uint16_t* v_cache,
+                         const uint16_t* k_self, const uint16_t* v_self, const float* o_part,
+                         const float* lse_part, int32_t n_parts, Phase2Geometry* out) {
+  const int has_self = k_self != nullptr || v_self != nullptr;
+  const int32_t want = pulsar_phase2_num_parts(a, batch, n_shards, shard_len, q_len, has_self);
+  if (want <= 0) return want < 0 ? want : PULSAR_EINVAL;
+  if (n_parts != want) return PULSAR_EINVAL;
+  if (has_self && (!aligned16(k_self) || !aligned16(v_self))) return PULSAR_EINVAL;
+  if (!aligned16(qq) || !aligned16(o_part) || !lse_part) return PULSAR_EINVAL;
+  if (n_shards > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) return PULSAR_EINVAL;
+  if (n_shards > 0 && shard_len % 8 != 0) return PULSAR_EUNSUPPORTED;  // d-major value runs of 8
+  if (q_pos0 < 0) return PULSAR_EINVAL;
+  if ((int64_t)batch * n_shards * shard_len * a->n_kv_heads > INT32_MAX) return PULSAR_EUNSUPPORTED;
+  if ((int64_t)batch * q_len > INT32_MAX / 2) return PULSAR_EUNSUPPORTED;
+  *out = phase2_geometry(batch, n_shards, n_shards > 0 ? shard_len : 1, q_len, a->n_q_heads,
+                         a->n_kv_heads, a->head_dim, has_self);
+  if (!phase2_grid_ok(*out)) return PULSAR_EUNSUPPORTED;
+  return PULSAR_OK;
+}
+
+// Preparation and attention launches of a checked Phase-2 query over the
+// workspace at w (layout2(pg).total bytes).
+int phase2_query_launch(const pulsar_attn* a, const Phase2Geometry& pg, const uint16_t* qq,
+                        int64_t q_pos0, const uint16_t* k_cache, const uint16_t* v_cache,
+                        const uint16_t* k_self, const uint16_t* v_self, float* o_part,
+                        float* lse_part, char* w, hipStream_t s) {
+  const bool has_self = pg.has_self != 0;
+  const Layout2 l = layout2(pg);
+  uint16_t* q_rot = reinterpret_cast<uint16_t*>(w + l.q_rot);
+  uint16_t* k_rot = has_self ? reinterpret_cast<uint16_t*>(w + l.k_rot) : nullptr;
+  uint16_t* v_t = has_self ? reinterpret_cast<uint16_t*>(w + l.v_t) : nullptr;
+  if (launch_phase2_prep(qq, has_self ? k_self : nullptr, v_self, pg.batch, pg.q_len,
+                         a->n_q_heads, a->n_kv_heads, a->head_dim, q_pos0, a->rope_base,
+                         a->rope_scaling, pg.self_pad, q_rot, k_rot, v_t, s))
+    return PULSAR_EHIP;
+  SelfShard self{};
+  if (has_self) {
+    self.k = k_rot;
+    self.v = v_t;
+    self.k_seq = (int64_t)pg.q_len * a->n_kv_heads * a->head_dim;
+    self.v_seq = (int64_t)a->n_kv_heads * a->head_dim * pg.self_pad;
+    self.n = pg.q_len;
+    self.v_ld = pg.self_pad;
+  }
+  return launch_phase2(pg, q_rot, k_cache, v_cache, self, o_part, lse_part, s) == 0 ? PULSAR_OK
+                                                                                       : PULSAR_EHIP;
+}
+
+// Scratch of pulsar_phase2_query_noalloc: the workspace of the Phase-2 query
+// (rotated query, rotated self keys, d-major self values) in one fixed device
+// array, so that the call allocates nothing.  Each device holds its own copy at
+// its own address; in host code `scratch` names a host-side stand-in, so kernels
+// are only ever given the device address hipGetSymbolAddress returns, looked up
+// once per device (with that device current) and kept.  Every call on a device
+// shares that device's array: calls that overlap on one device race.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices];
+
+int noalloc_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PULSAR_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return PULSAR_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PULSAR_EHIP;
+    g_scratch_dev[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return PULSAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -341,44 +422,34 @@ int pulsar_phase2_query(const pulsar_attn* a, int32_t batch, int32_t n_shards, i
                         const uint16_t* k_cache, const uint16_t* v_cache, const uint16_t* k_self,
                         const uint16_t* v_self, float* o_part, float* lse_part, int32_t n_parts,
                         void* ws, size_t ws_bytes, void* stream) {
-  const int has_self = k_self != nullptr || v_self != nullptr;
-  const int32_t want = pulsar_phase2_num_parts(a, batch, n_shards, shard_len, q_len, has_self);
-  if (want <= 0) return want < 0 ? want : PULSAR_EINVAL;
-  if (n_parts != want) return PULSAR_EINVAL;
-  if (has_self && (!aligned16(k_self) || !aligned16(v_self))) return PULSAR_EINVAL;
-  if (!aligned16(qq) || !aligned16(o_part) || !lse_part) return PULSAR_EINVAL;
-  if (n_shards > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) return PULSAR_EINVAL;
-  if (n_shards > 0 && shard_len % 8 != 0) return PULSAR_EUNSUPPORTED;  // d-major value runs of 8
-  if (q_pos0 < 0) return PULSAR_EINVAL;
-  if ((int64_t)batch * n_shards * shard_len * a->n_kv_heads > INT32_MAX) return PULSAR_EUNSUPPORTED;
-  Phase2Geometry pg = phase2_geometry(batch, n_shards, n_shards > 0 ? shard_len : 1, q_len,
-                                      a->n_q_heads, a->n_kv_heads, a->head_dim, has_self);
-  if (!phase2_grid_ok(pg)) return PULSAR_EUNSUPPORTED;
-  const Layout2 l = layout2(pg);
-  if (!ws || ws_bytes < l.total) return PULSAR_EWORKSPACE;
+  Phase2Geometry pg;
+  int rc = phase2_query_checked(a, batch, n_shards, shard_len, qq, q_len, q_pos0, k_cache,
+                                v_cache, k_self, v_self, o_part, lse_part, n_parts, &pg);
+  if (rc) return rc;
+  if (!ws || ws_bytes < layout2(pg).total) return PULSAR_EWORKSPACE;
   if (!aligned16(ws)) return PULSAR_EINVAL;
-  char* w = static_cast<char*>(ws);
-  uint16_t* q_rot = reinterpret_cast<uint16_t*>(w + l.q_rot);
-  uint16_t* k_rot = has_self ? reinterpret_cast<uint16_t*>(w + l.k_rot) : nullptr;
-  uint16_t* v_t = has_self ? reinterpret_cast<uint16_t*>(w + l.v_t) : nullptr;
-  hipStream_t s = as_stream(stream);
-  if ((int64_t)batch * q_len > INT32_MAX / 2) return PULSAR_EUNSUPPORTED;
-  if (launch_phase2_prep(qq, has_self ? k_self : nullptr, v_self, batch, q_len, a->n_q_heads,
-                         a->n_kv_heads, a->head_dim, q_pos0, a->rope_base, a->rope_scaling, pg.self_pad, q_rot,
-                         k_rot, v_t, s))
-    return PULSAR_EHIP;
-  SelfShard self{};
-  if (has_self) {
-    self.k = k_rot;
-    self.v = v_t;
-    self.k_seq = (int64_t)q_len * a->n_kv_heads * a->head_dim;
-    self.v_seq = (int64_t)a->n_kv_heads * a->head_dim * pg.self_pad;
-    self.n = q_len;
-    self.v_ld = pg.self_pad;
-  }
-  return launch_phase2(pg, q_rot, k_cache, v_cache, self, o_part, lse_part, s) == 0 ? PULSAR_OK
-                                                                                       : PULSAR_EHIP;
+  return phase2_query_launch(a, pg, qq, q_pos0, k_cache, v_cache, k_self, v_self, o_part,
+                             lse_part, static_cast<char*>(ws), as_stream(stream));
 }
+
+int pulsar_phase2_query_noalloc(const pulsar_attn* a, int32_t batch, int32_t n_shards,
+                                int32_t shard_len, const uint16_t* qq, int32_t q_len,
+                                int64_t q_pos0, const uint16_t* k_cache, const uint16_t* v_cache,
+                                const uint16_t* k_self, const uint16_t* v_self, float* o_part,
+                                float* lse_part, int32_t n_parts, void* stream) {
+  Phase2Geometry pg;
+  int rc = phase2_query_checked(a, batch, n_shards, shard_len, qq, q_len, q_pos0, k_cache,
+                                v_cache, k_self, v_self, o_part, lse_part, n_parts, &pg);
+  if (rc) return rc;
+  if (layout2(pg).total > kNoAllocScratchBytes) return PULSAR_EUNSUPPORTED;
+  char* w = nullptr;
+  rc = noalloc_scratch(&w);
+  if (rc) return rc;
+  return phase2_query_launch(a, pg, qq, q_pos0, k_cache, v_cache, k_self, v_self, o_part,
+                             lse_part, w, as_stream(stream));
+}
+
+size_t pulsar_phase2_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
 
 int pulsar_self_append(const pulsar_attn* a, int32_t batch, int32_t cap, int32_t n_self,
                        int32_t n_new, int64_t self_pos0, const uint16_t* k_new,

@@ -237,3 +237,30 @@ def test_generation_calls_reject_bad_arguments():
     assert dec(1, 120, 0) == B.PULSAR_EINVAL               # fewer self tokens than queries
     assert dec(1, 124, 65) == B.PULSAR_EUNSUPPORTED        # capacity not a multiple of 8
     assert dec(1, 128, 65, wsb=ws - 1) == B.PULSAR_EWORKSPACE
+
+
+@needs_lib
+def test_noalloc_query_rejects_on_the_host():
+    """The no-allocation Phase-2 query validates like pulsar_phase2_query, and
+    rejects a workspace larger than its fixed array before touching a device."""
+    lib = B.lib()
+    cap = B.pulsar_phase2_noalloc_max_bytes()
+    assert cap == 8 << 20
+    A = ctypes.byref(ATTN)
+
+    def q2(batch, q_len, n_parts, has_self=True, pos0=131072):
+        s = FAKE if has_self else None
+        return lib.pulsar_phase2_query_noalloc(A, batch, 8, 16384, FAKE, q_len, pos0, FAKE, FAKE, s,
+                                               s, FAKE, FAKE, n_parts, None)
+
+    fits = max(q for q in range(1, 2000) if B.pulsar_phase2_workspace_bytes(ATTN, 1, q, True) <= cap)
+    assert fits == 678
+    n_big = B.pulsar_phase2_num_parts(ATTN, 1, 8, 16384, fits + 1, True)
+    assert q2(1, fits + 1, n_big) == B.PULSAR_EUNSUPPORTED       # workspace above the array
+    n8 = B.pulsar_phase2_num_parts(ATTN, 8, 8, 16384, 100, True)
+    assert q2(8, 100, n8) == B.PULSAR_EUNSUPPORTED               # 800 tokens of batch 8
+    n = B.pulsar_phase2_num_parts(ATTN, 1, 8, 16384, 64, True)
+    assert q2(1, 64, n + 1) == B.PULSAR_EINVAL                   # wrong part count
+    assert q2(1, 64, n, pos0=-1) == B.PULSAR_EINVAL
+    assert lib.pulsar_phase2_query_noalloc(A, 1, 8, 16384, FAKE, 64, 0, FAKE, FAKE, FAKE, None,
+                                           FAKE, FAKE, n, None) == B.PULSAR_EINVAL
