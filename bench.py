@@ -33,37 +33,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="128k", help="tiny | 32k | 128k | 128k_star | 512k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="oracle Phase-1 rows timed on the host")
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="Phase-1 rows of the last block the oracle recomputes on the host")
     ap.add_argument("--gen-tokens", type=int, default=128,
                     help="generated tokens timed after the main steps (0: none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (counter calibration)")
     return ap.parse_args()
-
-
-KERNEL_SOURCES = ("attn.hip", "common.hpp")
-
-
-def code_text(src: str) -> str:
-    """C++ source without comments and with whitespace collapsed: what the
-    compiler sees (string literals in these sources hold no comment markers)."""
-    import re
-    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-    src = re.sub(r"//[^\n]*", " ", src)
-    return " ".join(src.split())
-
-
-def kernel_source_hash():
-    """Hash of the attention kernels' code (comments and layout ignored): counter
-    readings taken on other code no longer describe the kernel and are not
-    reported."""
-    import hashlib
-    h = hashlib.sha256()
-    d = os.path.join(ROOT, "long_context_blockwise_max_amd", "csrc")
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(d, f), encoding="utf-8") as fh:
-            h.update(code_text(fh.read()).encode())
-    return h.hexdigest()[:16]
 
 
 def recorded_traffic(workload, kernel):
@@ -76,6 +52,7 @@ def recorded_traffic(workload, kernel):
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
+    from long_context_blockwise_max_amd.source_hash import kernel_source_hash
     if rec.get("source_hash") != kernel_source_hash():
         return None
     ent = rec.get("kernels", {}).get(workload, {}).get(kernel)
@@ -181,27 +158,61 @@ def generation(path, w, n_tokens, stream):
             "warm_cache": True}
 
 
-def cpu_baseline(w, tok, q_bits, k_bits, v_bits, n_rows):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    Phase-1 rows of the last block (the longest prefix), all heads, including
-    the rotation of every key those rows see.  Returns a rate in TFLOP/s."""
+def host_description():
+    """CPU model of this host and the BLAS numpy was built against."""
+    import numpy as np
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        dep = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{dep.get('name')} {dep.get('version', '')}".strip()
+    except Exception:       # numpy builds without the dict form
+        pass
+    return model, blas
+
+
+def snapshot_outputs(path, w, rows):
+    """GPU results of the last benched step, copied to the host before anything
+    else runs: the selection, the Phase-1 outputs of `rows` ((block, row) pairs)
+    and the merged Phase-2 answer of sequence 0."""
+    import torch
+    pos = torch.tensor([i * w.block_size + r for i, r in rows], device=path.o.device)
+    return {"sel": path.sel[:, :w.k_eff].cpu().numpy(),
+            "o_rows": path.o.index_select(0, pos).cpu().numpy(),
+            "o_q": path.o_q[0].cpu().numpy(), "lse_q": path.lse_q[0].cpu().numpy()}
+
+
+def parity_rows(w, n_rows):
+    """(block, row) pairs the Phase-1 oracle recomputes: n_rows seeded rows of
+    the last block (the longest prefix), its first and last rows included."""
+    import numpy as np
+    rng = np.random.default_rng(0)
+    i = w.n_blocks - 1
+    rows = set(int(r) for r in rng.choice(w.block_size, size=max(0, n_rows - 2), replace=False))
+    rows |= {0, w.block_size - 1}
+    return [(i, r) for r in sorted(rows)]
+
+
+def cpu_baseline(w, tok, q_bits, k_bits, v_bits, qq, kq, vq, gpu, rows, p1_flops):
+    """The CPU oracle, as it stands, on the benched inputs: the whole Max-IDF
+    selection; the rotation of every context key into the retained cache and the
+    whole Phase-2 query + merge of sequence 0; Phase-1 rows `rows` of the last
+    block, all heads, timed and extrapolated (labelled) to the whole Phase-1
+    FLOP count.  Its outputs are also compared with the GPU's results of the
+    benched step (`gpu`, from snapshot_outputs).  Value: the Phase-1 rate."""
     import numpy as np
 
     import workloads as W
     from oracle import attention as OA
     from oracle import selection as OS
-
-    t0 = time.perf_counter()
-    sel, _, _ = OS.select(tok, w.n_blocks, w.block_size, w.chunk_size, w.budget_chunks, w.vocab_size)
-    pre = OS.prefix_positions(sel, w.n_blocks, w.block_size, w.chunk_size, w.sink_size)
-    i = w.n_blocks - 1
-    rng = np.random.default_rng(0)
-    rows = sorted(int(r) for r in rng.choice(w.block_size, size=n_rows, replace=False))
-    r_max = max(rows)
-    keys = np.concatenate([pre[i], np.arange(i * w.block_size, i * w.block_size + r_max + 1)])
-    khat = np.zeros((w.context_len, w.n_kv_heads, w.head_dim), np.float32)
-    uk = np.unique(keys)
-    khat[uk] = OA.rotate_bf16(W.bf16_bits_to_f64(k_bits[uk]), uk, w.rope_base)
 
     class Rows:
         def __init__(self, bits):
@@ -210,20 +221,76 @@ def cpu_baseline(w, tok, q_bits, k_bits, v_bits, n_rows):
         def __getitem__(self, idx):
             return W.bf16_bits_to_f64(self.bits[idx])
 
-    OA.phase1_rows(Rows(q_bits), khat, Rows(v_bits), pre, [(i, r) for r in rows], w.block_size,
-                   w.rope_base)
-    dt = time.perf_counter() - t0
-    flops = sum(4.0 * w.head_dim * w.n_q_heads * (len(pre[i]) + r + 1) for r in rows)
+    t0 = time.perf_counter()
+    sel, _, _ = OS.select(tok, w.n_blocks, w.block_size, w.chunk_size, w.budget_chunks, w.vocab_size)
+    t_sel = time.perf_counter() - t0
+    pre = OS.prefix_positions(sel, w.n_blocks, w.block_size, w.chunk_size, w.sink_size)
+
+    t0 = time.perf_counter()
+    khat = np.empty(k_bits.shape, np.float32)
+    step = 8192
+    for s0 in range(0, w.context_len, step):
+        kb = W.bf16_bits_to_f64(k_bits[s0:s0 + step])
+        khat[s0:s0 + step] = OA.rotate_bf16(kb, np.arange(s0, s0 + kb.shape[0]), w.rope_base)
+    t_rope = time.perf_counter() - t0
+
+    t0 = time.perf_counter()
+    kc = khat.reshape(w.n_blocks, w.block_size, w.n_kv_heads, w.head_dim).transpose(0, 2, 1, 3)
+    vc = W.bf16_bits_to_f64(v_bits).reshape(w.n_blocks, w.block_size, w.n_kv_heads,
+                                            w.head_dim).transpose(0, 2, 1, 3)
+    parts = OA.phase2_partials(W.bf16_bits_to_f64(qq[0]), w.context_len, kc, vc,
+                               W.bf16_bits_to_f64(kq[0]), W.bf16_bits_to_f64(vq[0]), w.rope_base)
+    want_o, want_lse = OA.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+    t_p2 = time.perf_counter() - t0
+    del vc, parts
+
+    i = w.n_blocks - 1
+    t0 = time.perf_counter()
+    want_rows = OA.phase1_rows_in_block(Rows(q_bits), khat, Rows(v_bits), pre[i], i,
+                                        [r for _, r in rows], w.block_size, w.rope_base)
+    t_p1 = time.perf_counter() - t0
+    flops = sum(4.0 * w.head_dim * w.n_q_heads * (len(pre[i]) + r + 1) for _, r in rows)
+    rate = flops / t_p1
+
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
+    model, blas = host_description()
+
+    def err(got, want):
+        e = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
+        return {"max_abs": float(f"{e.max():.3e}"), "mean_abs": float(f"{e.mean():.3e}")}
+
+    parity = {
+        "selection_bit_exact": bool(np.array_equal(gpu["sel"], sel)),
+        "phase1_rows": dict(err(gpu["o_rows"], want_rows), rows=len(rows), heads=w.n_q_heads,
+                            block=i),
+        "phase2_o": err(gpu["o_q"], want_o),
+        "phase2_lse": err(gpu["lse_q"], want_lse),
+        "tolerance": {"max_abs": 1e-2, "mean_abs": 1e-3, "lse_abs": 1e-3},
+    }
+    parity["within_tolerance"] = bool(
+        parity["selection_bit_exact"]
+        and all(parity[k]["max_abs"] <= 1e-2 and parity[k]["mean_abs"] <= 1e-3
+                for k in ("phase1_rows", "phase2_o"))
+        and parity["phase2_lse"]["max_abs"] <= 1e-3)
+    p1_full = p1_flops / rate
     return {
-        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-        "sample": (f"Phase-1 oracle (float64 numpy) on {n_rows} seeded rows of block {i} of the "
-                   f"{w.name} workload, all {w.n_q_heads} heads, incl. selection and key rotation; "
-                   f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s"),
-        "seconds": dt,
+        "value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": (f"float64 numpy oracle on the benched {w.name} inputs: Phase-1 rate from "
+                   f"{len(rows)} rows of block {i} (the longest prefix), all {w.n_q_heads} heads, "
+                   f"{flops / 1e9:.1f} GFLOP in {t_p1:.1f} s; plus the whole selection, key "
+                   f"rotation and Phase-2 query + merge of sequence 0"),
+        "cpu_model": model, "blas": blas,
+        "select_s": round(t_sel, 3), "rope_cache_s": round(t_rope, 3),
+        "phase2_merge_s": round(t_p2, 3),
+        "phase1_sample_s": round(t_p1, 3),
+        "phase1_full_s_extrapolated": round(p1_full, 1),
+        "step_s_extrapolated": round(t_sel + t_rope + p1_full + t_p2, 1),
+        "extrapolation": ("Phase-1 seconds = its algorithmic FLOPs / the sampled rows' rate; "
+                          "the other parts are timed whole"),
+        "parity": parity,
     }
 
 
@@ -302,6 +369,8 @@ def main():
         for j, n in enumerate(names):
             per[n].append(e[j].elapsed_time(e[j + 1]))
     avg = {n: float(np.mean(per[n])) for n in names}
+    rows = parity_rows(w, args.cpu_rows)
+    gpu_out = None if args.no_cpu_baseline else snapshot_outputs(path, w, rows)
     step_ms = wall * 1e3 / args.steps
     print(f"[bench] per-call ms: {avg}", file=sys.stderr, flush=True)
 
@@ -367,10 +436,9 @@ def main():
     if args.gen_tokens > 0:
         out["generation"] = generation(path, w, args.gen_tokens, stream)
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cb = cpu_baseline(w, tok, q_bits, k_bits, v_bits, args.cpu_rows)
-        cb.pop("seconds")
-        cb["value"] = round(cb["value"], 6)
+        print("[bench] timing the CPU oracle on the benched inputs", file=sys.stderr, flush=True)
+        cb = cpu_baseline(w, tok, q_bits, k_bits, v_bits, qq, kq, vq, gpu_out, rows, p1_flops)
+        out["parity"] = cb.pop("parity")
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 

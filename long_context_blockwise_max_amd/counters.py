@@ -13,7 +13,7 @@ KiB to bytes that really crossed the memory interface, applied to every kernel.
         --summary profiles/hbm_traffic_128k.md --command "<the rocprofv3 lines>"
 
 The JSON keeps the hash of the attention kernels' code (comments ignored) the counters were
-taken on; bench.py reports the traffic only while that hash still matches.
+taken on; the benchmark reports the traffic only while that hash still matches.
 """
 from __future__ import annotations
 
@@ -108,8 +108,9 @@ def main(argv=None):
 
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     sys.path.insert(0, root)
-    import bench
     import workloads as W
+
+    from .source_hash import kernel_source_hash
 
     fetch = per_dispatch(a.fetch, "FETCH_SIZE")
     write = per_dispatch(a.write, "WRITE_SIZE")
@@ -138,7 +139,7 @@ def main(argv=None):
     if os.path.exists(a.out):
         with open(a.out) as fh:
             rec = json.load(fh)
-    src = bench.kernel_source_hash()
+    src = kernel_source_hash()
     if rec.get("source_hash") != src:
         rec = {"kernels": {}}
     rec["source_hash"] = src

@@ -3,7 +3,7 @@ copy-kernel calibration, and the source-hash gate bench.py applies."""
 import csv
 import json
 
-import bench
+from long_context_blockwise_max_amd import source_hash as SH
 from long_context_blockwise_max_amd import counters
 
 HEAD = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
@@ -39,7 +39,7 @@ def test_summary_scales_by_copy_and_gates_on_source(tmp_path):
     assert e["dispatches"] == 2
     assert e["fetch_bytes"] == 2500 * 1024          # fetch scale 1.0
     assert e["write_bytes"] == 200 * 1024 * 2       # write scale 2.0
-    assert rec["source_hash"] == bench.kernel_source_hash()
+    assert rec["source_hash"] == SH.kernel_source_hash()
     assert "phase1_kernel" in md.read_text()
 
 
@@ -102,6 +102,6 @@ def test_code_hash_ignores_comments_and_layout():
     a = "int f(int x) {  // doubles\n  return 2 * x; /* plain */ }\n"
     b = "int f(int x) {\n  // twice x\n  return 2 * x;\n}\n"
     c = "int f(int x) { return 3 * x; }"
-    assert bench.code_text(a) == bench.code_text(b)
-    assert bench.code_text(a) != bench.code_text(c)
-    assert "s_waitcnt vmcnt(0)" in bench.code_text('asm volatile("s_waitcnt vmcnt(0)");  // wait')
+    assert SH.code_text(a) == SH.code_text(b)
+    assert SH.code_text(a) != SH.code_text(c)
+    assert "s_waitcnt vmcnt(0)" in SH.code_text('asm volatile("s_waitcnt vmcnt(0)");  // wait')
