@@ -164,8 +164,11 @@ int pulsar_select(const pulsar_geom* g, const int32_t* tok, int32_t* sel, int32_
   char* w = static_cast<char*>(ws);
   int32_t* status = reinterpret_cast<int32_t*>(w + l.status);
   int32_t* dfp = df ? df : reinterpret_cast<int32_t*>(w + l.df);
+  // chunk scores land in chunk_min_df when the caller wants them, else in the
+  // workspace's per-chunk rank area (used only by the other selection methods)
+  int32_t* scores = chunk_min_df ? chunk_min_df : reinterpret_cast<int32_t*>(w + l.ranks);
   return launch_select(tok, g->n_blocks, g->block_size, g->chunk_size, kept, g->vocab_size, sel,
-                       chunk_min_df, dfp, status, as_stream(stream)) == 0
+                       scores, dfp, status, as_stream(stream)) == 0
              ? PULSAR_OK
              : PULSAR_EHIP;
 }

@@ -6,8 +6,10 @@
 
 namespace pulsar {
 
+// chunk_score [N][n_chunks]: receives every chunk's min df (the caller's
+// chunk_min_df output or workspace scratch)
 int launch_select(const int32_t* tok, int32_t n_blocks, int32_t block_size, int32_t chunk_size,
-                  int32_t kept, int32_t vocab, int32_t* sel, int32_t* chunk_min_df, int32_t* df,
+                  int32_t kept, int32_t vocab, int32_t* sel, int32_t* chunk_score, int32_t* df,
                   int32_t* status, hipStream_t stream);
 
 // method 1 mean IDF, 2 entropy, 3 uniform (seeded), 4 evenly spaced.  Scratch:

@@ -7,15 +7,18 @@
 // kernels rank chunks by the integer min df: lower is better, the earlier
 // chunk wins among equals.  No floating point is involved.
 //
-// Three launches:
+// Four launches:
 //   select_clear    zero df[V] and the status word
 //   select_df       one workgroup per block: an LDS bitmap over the vocabulary
 //                   marks the block's distinct tokens; the lane that flips a
 //                   bit from 0 to 1 adds 1 to df[t] in global memory
-//   select_topk     one workgroup per block: chunk min-df into LDS, an LDS
-//                   histogram over the score range finds the cut-off score, and
-//                   wave ballots + mbcnt rank ties in chunk order and compact
-//                   the kept chunks in ascending order
+//   select_score    one lane per token over the whole context: the token's df,
+//                   then a min over the lanes of its chunk (the chunk's score),
+//                   so the df gathers run in parallel on every CU
+//   select_topk     one workgroup per block: the block's scores into LDS, an
+//                   LDS histogram over the score range finds the cut-off score,
+//                   and wave ballots + mbcnt rank ties in chunk order and
+//                   compact the kept chunks in ascending order
 #include <algorithm>
 
 #include "common.hpp"
@@ -33,26 +36,82 @@ __global__ void __launch_bounds__(256) select_clear(int32_t* __restrict__ df, in
   for (; i < vocab; i += (int64_t)gridDim.x * blockDim.x) df[i] = 0;
 }
 
-__global__ void __launch_bounds__(1024) select_df(const int32_t* __restrict__ tok, int32_t block_size,
-                                                  int32_t vocab, int32_t* __restrict__ df,
-                                                  int32_t* __restrict__ status) {
+constexpr int kDfThreads = 1024;
+constexpr int kDfBatch = 16;   // tokens a thread loads before its bitmap updates
+
+__global__ void __launch_bounds__(kDfThreads) select_df(const int32_t* __restrict__ tok,
+                                                        int32_t block_size, int32_t vocab,
+                                                        int32_t* __restrict__ df,
+                                                        int32_t* __restrict__ status) {
   extern __shared__ uint32_t bits[];  // ceil(vocab / 32) words
   const int nwords = (vocab + 31) >> 5;
   for (int w = threadIdx.x; w < nwords; w += blockDim.x) bits[w] = 0u;
   __syncthreads();
   const int32_t* t = tok + (int64_t)blockIdx.x * block_size;
   bool bad = false;
-  for (int p = threadIdx.x; p < block_size; p += blockDim.x) {
-    int32_t id = t[p];
-    if (id < 0 || id >= vocab) {
-      bad = true;
-      continue;
+  // tokens are loaded kDfBatch at a time (independent loads in flight together),
+  // then marked; an id outside [0, V) is skipped and flagged
+  for (int p0 = 0; p0 < block_size; p0 += kDfThreads * kDfBatch) {
+    int32_t ids[kDfBatch];
+#pragma unroll
+    for (int e = 0; e < kDfBatch; ++e) {
+      const int p = p0 + e * kDfThreads + (int)threadIdx.x;
+      ids[e] = p < block_size ? t[p] : -1;
     }
-    uint32_t m = 1u << (id & 31);
-    uint32_t old = atomicOr(&bits[id >> 5], m);
-    if (!(old & m)) atomicAdd(&df[id], 1);
+#pragma unroll
+    for (int e = 0; e < kDfBatch; ++e) {
+      const int p = p0 + e * kDfThreads + (int)threadIdx.x;
+      const int32_t id = ids[e];
+      if (p >= block_size) continue;
+      if (id < 0 || id >= vocab) {
+        bad = true;
+        continue;
+      }
+      const uint32_t m = 1u << (id & 31);
+      const uint32_t old = atomicOr(&bits[id >> 5], m);
+      if (!(old & m)) atomicAdd(&df[id], 1);
+    }
   }
   if (bad) atomicOr(status, 1);
+}
+
+// Chunk scores (min df over the chunk; n_blocks + 1 for a chunk with no valid
+// token, so it ranks last) of the whole context, score[j * n_chunks + c].
+// CS = chunk size when it divides the wave (8, 16, 32 or 64): one lane per
+// token, a min over each group of CS lanes.  CS = 0: any chunk size, one thread
+// per chunk.
+template <int CS>
+__global__ void __launch_bounds__(256) select_score(const int32_t* __restrict__ tok,
+                                                    const int32_t* __restrict__ df, int64_t L,
+                                                    int32_t chunk_size, int32_t n_blocks,
+                                                    int32_t vocab, int32_t* __restrict__ score) {
+  const int big = n_blocks + 1;
+  if constexpr (CS > 0) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // token
+    int v = big;
+    if (p < L) {
+      const int32_t id = tok[p];
+      if (id >= 0 && id < vocab) v = df[id];
+    }
+#pragma unroll
+    for (int off = CS / 2; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
+    if (p < L && (p % CS) == 0) score[p / CS] = v;
+  } else {
+    const int64_t n = L / chunk_size;
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= n) return;
+    const int32_t* ct = tok + c * chunk_size;
+    int v = big;
+    for (int e0 = 0; e0 < chunk_size; e0 += 8) {
+      int32_t ids[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ids[e] = ct[e0 + e];   // chunk_size is a multiple of 8
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (ids[e] >= 0 && ids[e] < vocab) v = min(v, df[ids[e]]);
+    }
+    score[c] = v;
+  }
 }
 
 // exclusive prefix of `pred` over the workgroup's threads in thread order;
@@ -77,34 +136,24 @@ __device__ __forceinline__ int wg_exclusive_count(bool pred, int* wave_tot, int*
 }
 
 __global__ void __launch_bounds__(kSelThreads) select_topk(
-    const int32_t* __restrict__ tok, const int32_t* __restrict__ df, int32_t n_blocks,
-    int32_t block_size, int32_t chunk_size, int32_t kept, int32_t vocab,
-    int32_t* __restrict__ sel, int32_t* __restrict__ chunk_min_df) {
+    const int32_t* __restrict__ chunk_score, int32_t n_blocks, int32_t n_chunks, int32_t kept,
+    int32_t* __restrict__ sel) {
   extern __shared__ int32_t lds[];
-  const int n_chunks = block_size / chunk_size;
   int32_t* score = lds;                    // [n_chunks]
   int32_t* hist = lds + n_chunks;          // [n_blocks + 2]
   __shared__ int wave_tot[kSelWaves];
   __shared__ int cut[2];                   // cut-off score, ties still needed
   const int j = blockIdx.x;
-  const int32_t* t = tok + (int64_t)j * block_size;
   const int big = n_blocks + 1;            // a chunk with no valid token ranks last
 
   for (int h = threadIdx.x; h < n_blocks + 2; h += blockDim.x) hist[h] = 0;
   __syncthreads();
   for (int c = threadIdx.x; c < n_chunks; c += blockDim.x) {
-    int mn = big;
-    const int32_t* ct = t + c * chunk_size;
-    for (int e = 0; e < chunk_size; ++e) {
-      int32_t id = ct[e];
-      if (id >= 0 && id < vocab) mn = min(mn, df[id]);
-    }
+    const int mn = chunk_score[(int64_t)j * n_chunks + c];
     score[c] = mn;
     atomicAdd(&hist[mn], 1);
-    if (chunk_min_df) chunk_min_df[(int64_t)j * n_chunks + c] = mn;
   }
   __syncthreads();
-  if (kept <= 0) return;
   if (threadIdx.x == 0) {
     int cum = 0, th = big;
     for (int s = 0; s <= big; ++s) {
@@ -134,7 +183,7 @@ __global__ void __launch_bounds__(kSelThreads) select_topk(
 }
 
 int launch_select(const int32_t* tok, int32_t n_blocks, int32_t block_size, int32_t chunk_size,
-                  int32_t kept, int32_t vocab, int32_t* sel, int32_t* chunk_min_df, int32_t* df,
+                  int32_t kept, int32_t vocab, int32_t* sel, int32_t* chunk_score, int32_t* df,
                   int32_t* status, hipStream_t stream) {
   int clear_blocks = (int)std::min<int64_t>(1024, ((int64_t)vocab + 255) / 256);
   hipLaunchKernelGGL(select_clear, dim3(clear_blocks), dim3(256), 0, stream, df, vocab, status);
@@ -143,16 +192,32 @@ int launch_select(const int32_t* tok, int32_t n_blocks, int32_t block_size, int3
       hipFuncSetAttribute(reinterpret_cast<const void*>(&select_df),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bitmap_bytes) != hipSuccess)
     return -3;
-  hipLaunchKernelGGL(select_df, dim3(n_blocks), dim3(1024), bitmap_bytes, stream, tok,
+  hipLaunchKernelGGL(select_df, dim3(n_blocks), dim3(kDfThreads), bitmap_bytes, stream, tok,
                      block_size, vocab, df, status);
-  int n_chunks = block_size / chunk_size;
-  size_t lds = (size_t)(n_chunks + n_blocks + 2) * 4;
-  if (lds > 65536 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&select_topk),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-    return -3;
-  hipLaunchKernelGGL(select_topk, dim3(n_blocks), dim3(kSelThreads), lds, stream, tok, df,
-                     n_blocks, block_size, chunk_size, kept, vocab, sel, chunk_min_df);
+  const int64_t L = (int64_t)n_blocks * block_size;
+  const int n_chunks = block_size / chunk_size;
+  if (64 % chunk_size == 0) {
+    const dim3 grid((unsigned)((L + 255) / 256));
+    switch (chunk_size) {
+      case 8: hipLaunchKernelGGL(select_score<8>, grid, dim3(256), 0, stream, tok, df, L, chunk_size, n_blocks, vocab, chunk_score); break;
+      case 16: hipLaunchKernelGGL(select_score<16>, grid, dim3(256), 0, stream, tok, df, L, chunk_size, n_blocks, vocab, chunk_score); break;
+      case 32: hipLaunchKernelGGL(select_score<32>, grid, dim3(256), 0, stream, tok, df, L, chunk_size, n_blocks, vocab, chunk_score); break;
+      default: hipLaunchKernelGGL(select_score<64>, grid, dim3(256), 0, stream, tok, df, L, chunk_size, n_blocks, vocab, chunk_score); break;
+    }
+  } else {
+    const int64_t n = L / chunk_size;
+    hipLaunchKernelGGL(select_score<0>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       tok, df, L, chunk_size, n_blocks, vocab, chunk_score);
+  }
+  if (kept > 0) {
+    size_t lds = (size_t)(n_chunks + n_blocks + 2) * 4;
+    if (lds > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&select_topk),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return -3;
+    hipLaunchKernelGGL(select_topk, dim3(n_blocks), dim3(kSelThreads), lds, stream, chunk_score,
+                       n_blocks, n_chunks, kept, sel);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

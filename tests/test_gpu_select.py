@@ -108,3 +108,35 @@ def test_select_is_deterministic():
     b = run_select(tok, w.n_blocks, w.block_size, w.chunk_size, w.budget_chunks, w.vocab_size)
     for x, y in zip(a[:3], b[:3]):
         np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("chunk", [8, 16, 24, 40, 64, 96])
+def test_select_chunk_sizes(chunk):
+    """Chunk sizes that divide the 64-lane wave (one lane per token, a min over
+    the chunk's lanes) and sizes that do not (one thread per chunk), with scores
+    spread over 1..N by a small vocabulary."""
+    n_blocks, n_chunks = 6, 40
+    b = chunk * n_chunks
+    tok = W.small_vocab_tokens(chunk, n_blocks, b, 96)
+    sel, cm, df, status = run_select(tok, n_blocks, b, chunk, 7, 96)
+    want_sel, want_df, _ = OS.select(tok, n_blocks, b, chunk, 7, 96)
+    np.testing.assert_array_equal(df, want_df)
+    np.testing.assert_array_equal(cm, OS.chunk_min_df(tok, want_df, n_blocks, b, chunk))
+    np.testing.assert_array_equal(sel, want_sel)
+    assert status == 0
+
+
+def test_select_without_chunk_scores_out():
+    """chunk_min_df = NULL: the scores go through the workspace; same selection."""
+    torch = torch_cuda()
+    from long_context_blockwise_max_amd import binding as B
+    tok = W.small_vocab_tokens(3, 5, 1024, 64)
+    g = B.make_geom(5, 1024, 32, 6, 64, 64)
+    dev = torch.device("cuda")
+    t = torch.from_numpy(np.ascontiguousarray(tok, dtype=np.int32)).to(dev)
+    sel = torch.full((5, 6), -7, dtype=torch.int32, device=dev)
+    ws = torch.full((B.pulsar_workspace_bytes(g, None),), 0xAB, dtype=torch.uint8, device=dev)
+    B.pulsar_select(g, t, sel, None, None, ws)
+    torch.cuda.synchronize()
+    want_sel, _, _ = OS.select(tok, 5, 1024, 32, 6, 64)
+    np.testing.assert_array_equal(sel.cpu().numpy(), want_sel)
