@@ -65,10 +65,11 @@ int check_pair(const pulsar_geom* g, const pulsar_attn* a) {
 }
 
 // select + phase 1 workspace: status word | df | chunk keys | chunk ranks |
-// rotated q | prefix lists | work order (keys and ranks serve the selection
-// methods other than Max-IDF)
+// block bitmaps | rotated q | prefix lists | work order (keys and ranks serve
+// the selection methods other than Max-IDF; Max-IDF keeps its chunk scores in
+// the ranks area when the caller does not ask for them)
 struct Layout {
-  size_t status, df, keys, ranks, q_rot, lists, order, total;
+  size_t status, df, keys, ranks, bits, q_rot, lists, order, total;
 };
 
 Layout layout(const pulsar_geom* g, const pulsar_attn* a) {
@@ -83,6 +84,8 @@ Layout layout(const pulsar_geom* g, const pulsar_attn* a) {
   off = align_up(off + chunks * 32);
   l.ranks = off;
   off = align_up(off + chunks * 4);
+  l.bits = off;
+  off = align_up(off + (size_t)g->n_blocks * ((g->vocab_size + 31) / 32) * 4);
   const int64_t L = (int64_t)g->n_blocks * g->block_size;
   l.q_rot = l.lists = l.order = off;
   if (a) {
@@ -163,12 +166,13 @@ int pulsar_select(const pulsar_geom* g, const int32_t* tok, int32_t* sel, int32_
   if (!aligned16(ws)) return PULSAR_EINVAL;
   char* w = static_cast<char*>(ws);
   int32_t* status = reinterpret_cast<int32_t*>(w + l.status);
-  int32_t* dfp = df ? df : reinterpret_cast<int32_t*>(w + l.df);
   // chunk scores land in chunk_min_df when the caller wants them, else in the
   // workspace's per-chunk rank area (used only by the other selection methods)
   int32_t* scores = chunk_min_df ? chunk_min_df : reinterpret_cast<int32_t*>(w + l.ranks);
+  int32_t* dfp = df ? df : reinterpret_cast<int32_t*>(w + l.df);
   return launch_select(tok, g->n_blocks, g->block_size, g->chunk_size, kept, g->vocab_size, sel,
-                       scores, dfp, status, as_stream(stream)) == 0
+                       scores, dfp, reinterpret_cast<uint32_t*>(w + l.bits), status,
+                       as_stream(stream)) == 0
              ? PULSAR_OK
              : PULSAR_EHIP;
 }

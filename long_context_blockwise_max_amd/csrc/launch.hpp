@@ -7,10 +7,11 @@
 namespace pulsar {
 
 // chunk_score [N][n_chunks]: receives every chunk's min df (the caller's
-// chunk_min_df output or workspace scratch)
+// chunk_min_df output or workspace scratch); df [V] (output or scratch); scratch: bits
+// [N][ceil(V / 32)] words
 int launch_select(const int32_t* tok, int32_t n_blocks, int32_t block_size, int32_t chunk_size,
                   int32_t kept, int32_t vocab, int32_t* sel, int32_t* chunk_score, int32_t* df,
-                  int32_t* status, hipStream_t stream);
+                  uint32_t* bits, int32_t* status, hipStream_t stream);
 
 // method 1 mean IDF, 2 entropy, 3 uniform (seeded), 4 evenly spaced.  Scratch:
 // df [vocab] (mean IDF), keys [N][n_chunks][8] (16-byte aligned), ranks

@@ -8,10 +8,10 @@
 // chunk wins among equals.  No floating point is involved.
 //
 // Four launches:
-//   select_clear    zero df[V] and the status word
-//   select_df       one workgroup per block: an LDS bitmap over the vocabulary
-//                   marks the block's distinct tokens; the lane that flips a
-//                   bit from 0 to 1 adds 1 to df[t] in global memory
+//   select_bits     one workgroup per block: an LDS bitmap over the vocabulary
+//                   marks the block's distinct valid tokens and is written out
+//                   whole (nothing to clear beforehand)
+//   select_df_sum   one lane per id: df[t] = the number of block bitmaps holding t
 //   select_score    one lane per token over the whole context: the token's df,
 //                   then a min over the lanes of its chunk (the chunk's score),
 //                   so the df gathers run in parallel on every CU
@@ -19,6 +19,7 @@
 //                   LDS histogram over the score range finds the cut-off score,
 //                   and wave ballots + mbcnt rank ties in chunk order and
 //                   compact the kept chunks in ascending order
+// (The mean-IDF method below counts df with select_clear and select_df instead.)
 #include <algorithm>
 
 #include "common.hpp"
@@ -75,45 +76,6 @@ __global__ void __launch_bounds__(kDfThreads) select_df(const int32_t* __restric
   if (bad) atomicOr(status, 1);
 }
 
-// Chunk scores (min df over the chunk; n_blocks + 1 for a chunk with no valid
-// token, so it ranks last) of the whole context, score[j * n_chunks + c].
-// CS = chunk size when it divides the wave (8, 16, 32 or 64): one lane per
-// token, a min over each group of CS lanes.  CS = 0: any chunk size, one thread
-// per chunk.
-template <int CS>
-__global__ void __launch_bounds__(256) select_score(const int32_t* __restrict__ tok,
-                                                    const int32_t* __restrict__ df, int64_t L,
-                                                    int32_t chunk_size, int32_t n_blocks,
-                                                    int32_t vocab, int32_t* __restrict__ score) {
-  const int big = n_blocks + 1;
-  if constexpr (CS > 0) {
-    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // token
-    int v = big;
-    if (p < L) {
-      const int32_t id = tok[p];
-      if (id >= 0 && id < vocab) v = df[id];
-    }
-#pragma unroll
-    for (int off = CS / 2; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
-    if (p < L && (p % CS) == 0) score[p / CS] = v;
-  } else {
-    const int64_t n = L / chunk_size;
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= n) return;
-    const int32_t* ct = tok + c * chunk_size;
-    int v = big;
-    for (int e0 = 0; e0 < chunk_size; e0 += 8) {
-      int32_t ids[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ids[e] = ct[e0 + e];   // chunk_size is a multiple of 8
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (ids[e] >= 0 && ids[e] < vocab) v = min(v, df[ids[e]]);
-    }
-    score[c] = v;
-  }
-}
-
 // exclusive prefix of `pred` over the workgroup's threads in thread order;
 // returns this thread's prefix and writes the workgroup total to *total.
 __device__ __forceinline__ int wg_exclusive_count(bool pred, int* wave_tot, int* total) {
@@ -133,6 +95,101 @@ __device__ __forceinline__ int wg_exclusive_count(bool pred, int* wave_tot, int*
   __syncthreads();
   *total = all;
   return before + in_wave;
+}
+
+// One workgroup per block: the block's distinct valid ids as a bitmap,
+// bits[j * words + t / 32] bit t % 32.  Block 0 also clears the status word.
+__global__ void __launch_bounds__(kDfThreads) select_bits(const int32_t* __restrict__ tok,
+                                                          int32_t block_size, int32_t vocab,
+                                                          uint32_t* __restrict__ bits_out,
+                                                          int32_t* __restrict__ status) {
+  extern __shared__ uint32_t bits[];  // ceil(vocab / 32) words
+  const int nwords = (vocab + 31) >> 5;
+  for (int w = threadIdx.x; w < nwords; w += blockDim.x) bits[w] = 0u;
+  if (threadIdx.x == 0 && blockIdx.x == 0) status[0] = 0;
+  __syncthreads();
+  const int32_t* t = tok + (int64_t)blockIdx.x * block_size;
+  for (int p0 = 0; p0 < block_size; p0 += kDfThreads * kDfBatch) {
+    int32_t ids[kDfBatch];
+#pragma unroll
+    for (int e = 0; e < kDfBatch; ++e) {
+      const int p = p0 + e * kDfThreads + (int)threadIdx.x;
+      ids[e] = p < block_size ? t[p] : -1;
+    }
+#pragma unroll
+    for (int e = 0; e < kDfBatch; ++e) {
+      if (ids[e] < 0 || ids[e] >= vocab) continue;
+      // frequent ids find their bit already set: a plain read spares the atomic
+      // (two lanes that both read it clear both set it, which is harmless)
+      const uint32_t m = 1u << (ids[e] & 31);
+      if (!(bits[ids[e] >> 5] & m)) atomicOr(&bits[ids[e] >> 5], m);
+    }
+  }
+  __syncthreads();
+  uint32_t* out = bits_out + (int64_t)blockIdx.x * nwords;
+  for (int w = threadIdx.x; w < nwords; w += blockDim.x) out[w] = bits[w];
+}
+
+// number of blocks whose bitmap holds id
+__device__ __forceinline__ int df_of(const uint32_t* __restrict__ bits, int nwords, int n_blocks,
+                                     int32_t id) {
+  const uint32_t* b = bits + (id >> 5);
+  const int sh = id & 31;
+  int c = 0;
+  for (int j = 0; j < n_blocks; ++j) c += (b[(int64_t)j * nwords] >> sh) & 1;
+  return c;
+}
+
+// df[t] = number of block bitmaps holding t, for every id t < vocab (lanes of a
+// wave read the same bitmap words)
+__global__ void __launch_bounds__(256) select_df_sum(const uint32_t* __restrict__ bits,
+                                                     int32_t n_blocks, int32_t vocab,
+                                                     int32_t* __restrict__ df) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < vocab) df[t] = df_of(bits, (vocab + 31) >> 5, n_blocks, (int32_t)t);
+}
+
+// Chunk scores (min df over the chunk; n_blocks + 1 for a chunk with no valid
+// token, so it ranks last) of the whole context, score[j * n_chunks + c].
+// CS = chunk size when it divides the wave (8, 16, 32 or 64): one lane per
+// token, a min over each group of CS lanes.  CS = 0: any chunk size, one thread
+// per chunk.
+template <int CS>
+__global__ void __launch_bounds__(256) select_score(const int32_t* __restrict__ tok,
+                                                    const int32_t* __restrict__ df, int64_t L,
+                                                    int32_t chunk_size, int32_t n_blocks,
+                                                    int32_t vocab, int32_t* __restrict__ score,
+                                                    int32_t* __restrict__ status) {
+  const int big = n_blocks + 1;
+  if constexpr (CS > 0) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // token
+    int v = big;
+    if (p < L) {
+      const int32_t id = tok[p];
+      if (id >= 0 && id < vocab) v = df[id];
+      else atomicOr(status, 1);   // an id outside [0, V): skipped, flagged
+    }
+#pragma unroll
+    for (int off = CS / 2; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off));
+    if (p < L && (p % CS) == 0) score[p / CS] = v;
+  } else {
+    const int64_t n = L / chunk_size;
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= n) return;
+    const int32_t* ct = tok + c * chunk_size;
+    int v = big;
+    for (int e0 = 0; e0 < chunk_size; e0 += 8) {
+      int32_t ids[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ids[e] = ct[e0 + e];   // chunk_size is a multiple of 8
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (ids[e] >= 0 && ids[e] < vocab) v = min(v, df[ids[e]]);
+        else atomicOr(status, 1);
+      }
+    }
+    score[c] = v;
+  }
 }
 
 __global__ void __launch_bounds__(kSelThreads) select_topk(
@@ -184,30 +241,30 @@ __global__ void __launch_bounds__(kSelThreads) select_topk(
 
 int launch_select(const int32_t* tok, int32_t n_blocks, int32_t block_size, int32_t chunk_size,
                   int32_t kept, int32_t vocab, int32_t* sel, int32_t* chunk_score, int32_t* df,
-                  int32_t* status, hipStream_t stream) {
-  int clear_blocks = (int)std::min<int64_t>(1024, ((int64_t)vocab + 255) / 256);
-  hipLaunchKernelGGL(select_clear, dim3(clear_blocks), dim3(256), 0, stream, df, vocab, status);
-  size_t bitmap_bytes = (size_t)((vocab + 31) / 32) * 4;
+                  uint32_t* bits, int32_t* status, hipStream_t stream) {
+  const size_t bitmap_bytes = (size_t)((vocab + 31) / 32) * 4;
   if (bitmap_bytes > 65536 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&select_df),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&select_bits),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bitmap_bytes) != hipSuccess)
     return -3;
-  hipLaunchKernelGGL(select_df, dim3(n_blocks), dim3(kDfThreads), bitmap_bytes, stream, tok,
-                     block_size, vocab, df, status);
+  hipLaunchKernelGGL(select_bits, dim3(n_blocks), dim3(kDfThreads), bitmap_bytes, stream, tok,
+                     block_size, vocab, bits, status);
+  hipLaunchKernelGGL(select_df_sum, dim3((unsigned)(((int64_t)vocab + 255) / 256)), dim3(256), 0,
+                     stream, bits, n_blocks, vocab, df);
   const int64_t L = (int64_t)n_blocks * block_size;
   const int n_chunks = block_size / chunk_size;
   if (64 % chunk_size == 0) {
     const dim3 grid((unsigned)((L + 255) / 256));
     switch (chunk_size) {
-      case 8: hipLaunchKernelGGL(select_score<8>, grid, dim3(256), 0, stream, tok, df, L, chunk_size, n_blocks, vocab, chunk_score); break;
-      case 16: hipLaunchKernelGGL(select_score<16>, grid, dim3(256), 0, stream, tok, df, L, chunk_size, n_blocks, vocab, chunk_score); break;
-      case 32: hipLaunchKernelGGL(select_score<32>, grid, dim3(256), 0, stream, tok, df, L, chunk_size, n_blocks, vocab, chunk_score); break;
-      default: hipLaunchKernelGGL(select_score<64>, grid, dim3(256), 0, stream, tok, df, L, chunk_size, n_blocks, vocab, chunk_score); break;
+      case 8: hipLaunchKernelGGL(select_score<8>, grid, dim3(256), 0, stream, tok, df, L, chunk_size, n_blocks, vocab, chunk_score, status); break;
+      case 16: hipLaunchKernelGGL(select_score<16>, grid, dim3(256), 0, stream, tok, df, L, chunk_size, n_blocks, vocab, chunk_score, status); break;
+      case 32: hipLaunchKernelGGL(select_score<32>, grid, dim3(256), 0, stream, tok, df, L, chunk_size, n_blocks, vocab, chunk_score, status); break;
+      default: hipLaunchKernelGGL(select_score<64>, grid, dim3(256), 0, stream, tok, df, L, chunk_size, n_blocks, vocab, chunk_score, status); break;
     }
   } else {
     const int64_t n = L / chunk_size;
     hipLaunchKernelGGL(select_score<0>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                       tok, df, L, chunk_size, n_blocks, vocab, chunk_score);
+                       tok, df, L, chunk_size, n_blocks, vocab, chunk_score, status);
   }
   if (kept > 0) {
     size_t lds = (size_t)(n_chunks + n_blocks + 2) * 4;
