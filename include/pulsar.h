@@ -308,6 +308,34 @@ int pulsar_phase2_decode(const pulsar_attn* a, int32_t batch, int32_t n_shards,
                          int32_t n_self, int64_t self_pos0, float* o_part, float* lse_part,
                          int32_t n_parts, void* ws, size_t ws_bytes, void* stream);
 
+/* One generation step as one call ("Dropping the Anchor ..." Section 2.2; the
+ * generated tokens of Section 5's --tokens_to_generate): the q_len new tokens
+ * are appended to the self caches, their queries attend to every retained shard
+ * and, causally, the self cache, and the parts are merged.  The same results,
+ * bit for bit, as pulsar_self_append (n_new = q_len) followed by
+ * pulsar_phase2_decode (n_self + q_len self tokens) and pulsar_lse_merge.  For
+ * one-token steps (every query row of a KV head in one wave, q_len <= 32) the
+ * attention launch appends the new tokens itself, so the step is two launches
+ * (attention, merge) instead of three.
+ *   qq, k_new, v_new     [B][q_len][H][d] bf16, pre-RoPE: the new tokens, at
+ *                        positions self_pos0 + n_self + t
+ *   k_self_cache, v_self_cache, cap   as for pulsar_self_append; they hold n_self
+ *                        tokens before the call and n_self + q_len after it
+ *   o_part, lse_part     [B][n_parts][q_len][Hq][d] / [B][n_parts][q_len][Hq]
+ *                        float32 scratch for the partials
+ *   n_parts              pulsar_phase2_num_parts(a, batch, n_shards, shard_len, q_len, 1)
+ *   o, lse               [B][q_len][Hq][d], [B][q_len][Hq] float32 out (lse may be NULL)
+ *   ws                   pulsar_decode_step_workspace_bytes(a, batch, q_len) bytes
+ * Errors: PULSAR_EINVAL, PULSAR_EWORKSPACE, PULSAR_EUNSUPPORTED, PULSAR_EHIP. */
+size_t pulsar_decode_step_workspace_bytes(const pulsar_attn* a, int32_t batch, int32_t q_len);
+int pulsar_decode_step(const pulsar_attn* a, int32_t batch, int32_t n_shards, int32_t shard_len,
+                       const uint16_t* qq, const uint16_t* k_new, const uint16_t* v_new,
+                       int32_t q_len, const uint16_t* k_cache, const uint16_t* v_cache,
+                       uint16_t* k_self_cache, uint16_t* v_self_cache, int32_t cap,
+                       int32_t n_self, int64_t self_pos0, float* o_part, float* lse_part,
+                       int32_t n_parts, float* o, float* lse, void* ws, size_t ws_bytes,
+                       void* stream);
+
 /* Exact log-sum-exp merge of partial attention results (the Star Attention
  * review's corrected update: weight exp(s_h - s_global) on the normalised A_h):
  *   lse = ln sum_p exp(lse_part[p]),  o = sum_p exp(lse_part[p] - lse) * o_part[p]

@@ -27,6 +27,7 @@ EXPORTED = (
     "pulsar_prefix_rows_len", "pulsar_phase1_prefix_rows",
     "pulsar_phase2_num_parts", "pulsar_phase2_workspace_bytes", "pulsar_phase2_query",
     "pulsar_phase2_query_noalloc", "pulsar_phase2_noalloc_max_bytes",
+    "pulsar_decode_step", "pulsar_decode_step_workspace_bytes",
     "pulsar_lse_merge", "pulsar_strerror",
 )
 
@@ -87,6 +88,11 @@ def lib():
         L.pulsar_phase2_query_noalloc.restype = ctypes.c_int
         L.pulsar_phase2_noalloc_max_bytes.argtypes = []
         L.pulsar_phase2_noalloc_max_bytes.restype = sz
+        L.pulsar_decode_step_workspace_bytes.argtypes = [A, i32, i32]
+        L.pulsar_decode_step_workspace_bytes.restype = sz
+        L.pulsar_decode_step.argtypes = [A, i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, i32, i32,
+                                         i64, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.pulsar_decode_step.restype = ctypes.c_int
         L.pulsar_prefix_rows_len.argtypes = [G]
         L.pulsar_prefix_rows_len.restype = i64
         L.pulsar_phase1_prefix_rows.argtypes = [G, A, vp, vp, vp, vp, sz, vp]
@@ -342,6 +348,32 @@ def pulsar_phase2_decode(attn: Attn, batch, n_shards, shard_len, qq, q_len, k_ca
         _ptr(lse_part, torch.float32, rows, "lse_part"), n_parts, _ptr(ws, torch.uint8, 0, "ws"),
         ws.numel(), _stream(stream))
     _check(rc, "pulsar_phase2_decode")
+
+
+def pulsar_decode_step_workspace_bytes(attn: Attn, batch, q_len) -> int:
+    return lib().pulsar_decode_step_workspace_bytes(ctypes.byref(attn), batch, q_len)
+
+
+def pulsar_decode_step(attn: Attn, batch, n_shards, shard_len, qq, k_new, v_new, q_len, k_cache,
+                       v_cache, k_self_cache, v_self_cache, cap, n_self, self_pos0, o_part,
+                       lse_part, n_parts, o, lse, ws, stream=None):
+    import torch
+    hq, hkv, d = attn.n_q_heads, attn.n_kv_heads, attn.head_dim
+    kv_n = batch * n_shards * hkv * shard_len * d
+    cache_n = batch * cap * hkv * d
+    rows = batch * n_parts * q_len * hq
+    rc = lib().pulsar_decode_step(
+        ctypes.byref(attn), batch, n_shards, shard_len, _bf16(qq, batch * q_len * hq * d, "qq"),
+        _bf16(k_new, batch * q_len * hkv * d, "k_new"), _bf16(v_new, batch * q_len * hkv * d, "v_new"),
+        q_len, _bf16(k_cache, kv_n, "k_cache", allow_none=n_shards == 0),
+        _bf16(v_cache, kv_n, "v_cache", allow_none=n_shards == 0),
+        _bf16(k_self_cache, cache_n, "k_self_cache"), _bf16(v_self_cache, cache_n, "v_self_cache"),
+        cap, n_self, int(self_pos0), _ptr(o_part, torch.float32, rows * d, "o_part"),
+        _ptr(lse_part, torch.float32, rows, "lse_part"), n_parts,
+        _ptr(o, torch.float32, batch * q_len * hq * d, "o"),
+        _ptr(lse, torch.float32, batch * q_len * hq, "lse", allow_none=True),
+        _ptr(ws, torch.uint8, 0, "ws"), ws.numel(), _stream(stream))
+    _check(rc, "pulsar_decode_step")
 
 
 def pulsar_lse_merge(batch, n_parts, q_len, n_q_heads, head_dim, o_part, lse_part, o, lse,

@@ -843,6 +843,14 @@ struct P2Args {
   int64_t q_pos0;
   double rope_base;
   int32_t rope_scaling;
+  // Generation step (decode form with q_raw only): k_new / v_new
+  // [B][lq][Hkv][D] pre-RoPE; the query tokens are the last lq self tokens and
+  // the launch appends them first (rotated keys into ks_w, values into the
+  // d-major vs_w).
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* ks_w;
+  uint16_t* vs_w;
 };
 
 // cos / sin table of the in-kernel query rotation: at most 32 tokens x D/2 pairs
@@ -852,11 +860,51 @@ struct QTab {
   static constexpr int BYTES = MAX_TOK * (D / 2) * 8;
 };
 
+// Generation step, append: self tokens tok_lo .. tok_hi - 1 (new tokens; token
+// tk is new token tk - (n_self - lq), at the query position of that index) of
+// sequence bb, KV head g, into the self caches: keys turned with the query
+// rotation table, values into their d-major columns; when tok_hi is the last
+// self token, the value columns after it up to the next multiple of 8 are
+// zeroed (the attention reads values in runs of 8 keys).  Called by the whole
+// workgroup, outside the attention loop (not inlined, so that its registers do
+// not add to the loop's).
+template <int D>
+__device__ __forceinline__ void append_self_tokens(const uint16_t* k_new, const uint16_t* v_new,
+                                                uint16_t* ks_w, uint16_t* vs_w, int64_t ks_seq,
+                                                int64_t vs_seq, int vs_ld, int n_self, int lq,
+                                                int hkv, const float2* tab, int bb, int g,
+                                                int tok_lo, int tok_hi) {
+  const int n_old = n_self - lq;
+  uint16_t* kdst = ks_w + (int64_t)bb * ks_seq + (int64_t)g * D;
+  uint16_t* vdst = vs_w + (int64_t)bb * vs_seq + (int64_t)g * D * vs_ld;
+  const int n_tok = tok_hi - tok_lo;
+  for (int e = threadIdx.x; e < n_tok * (D / 2); e += NTHR) {
+    const int tk = tok_lo + e / (D / 2), i = e % (D / 2), t = tk - n_old;
+    const uint16_t* src = k_new + (((int64_t)bb * lq + t) * hkv + g) * D;
+    const float2 cs = tab[t * (D / 2) + i];
+    float y1, y2;
+    rope_pair(bf16_to_f32(src[i]), bf16_to_f32(src[i + D / 2]), cs.x, cs.y, y1, y2);
+    uint16_t* kr = kdst + (int64_t)tk * hkv * D;
+    kr[i] = __builtin_bit_cast(uint16_t, (__bf16)y1);
+    kr[i + D / 2] = __builtin_bit_cast(uint16_t, (__bf16)y2);
+  }
+  for (int e = threadIdx.x; e < n_tok * D; e += NTHR) {
+    const int tk = tok_lo + e / D, d = e % D, t = tk - n_old;
+    vdst[(int64_t)d * vs_ld + tk] = v_new[(((int64_t)bb * lq + t) * hkv + g) * D + d];
+  }
+  if (tok_hi == n_self) {
+    const int pad = ((n_self + 7) & ~7) - n_self;
+    for (int e = threadIdx.x; e < D * pad; e += NTHR)
+      vdst[(int64_t)(e / pad) * vs_ld + n_self + e % pad] = 0;
+  }
+}
+
 // KSPLIT: the decode form (all query rows of the workgroup in one 32-row wave),
 // chosen by the launcher; two waves then split the subtiles of every tile.
-template <int D, bool KSPLIT>
+template <int D, bool KSPLIT, bool FUSED = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NTHR, NTHR), amdgpu_waves_per_eu(2, 2)))
 phase2_kernel(P2Args a) {
+  static_assert(!FUSED || KSPLIT, "the generation step's append runs in the decode form");
   constexpr int NQ = 1;
   // Tile slots.  The decode form streams its part from HBM with little work per
   // tile, so its loads run three tiles ahead (four slots, 128 KB at d = 128);
@@ -991,6 +1039,22 @@ phase2_kernel(P2Args a) {
       tab[e] = make_float2(c, sn);
     }
   }
+  if constexpr (FUSED) {
+    // Append the query tokens (self tokens n_self - lq .. n_self - 1) that lie in
+    // this part's self tiles, for KV head g, before this workgroup stages any
+    // tile, so that its own loads see them; no other workgroup reads those tiles.
+    const int64_t s_lo = (t0 > shard_tiles ? t0 : shard_tiles) - shard_tiles;
+    const int64_t s_hi = (t0 + n_tiles < all_tiles ? t0 + n_tiles : all_tiles) - shard_tiles;
+    const int n_old = a.n_self - a.lq;
+    const int tok_lo = (int)(s_lo * KT > n_old ? s_lo * KT : n_old);
+    const int tok_hi = (int)(s_hi * KT < a.n_self ? s_hi * KT : a.n_self);
+    if (tok_lo < tok_hi) {
+      __syncthreads();   // the table is written
+      append_self_tokens<D>(a.k_new, a.v_new, a.ks_w, a.vs_w, a.ks_seq, a.vs_seq, a.vs_ld, a.n_self,
+                            a.lq, a.hkv, tab, bb, g, tok_lo, tok_hi);
+      __syncthreads();   // the stores have completed before any tile load is issued
+    }
+  }
   // tiles past the part: the staging cursor stays on the last tile (staged into a
   // free slot, never read)
   Cur sc = first;
@@ -1123,8 +1187,13 @@ bool phase2_decode_form(const Phase2Geometry& g) {
 
 int launch_phase2(const Phase2Geometry& g, const uint16_t* q_rot, const uint16_t* k_cache,
                   const uint16_t* v_cache, const SelfShard& self, float* o_part,
-                  float* lse_part, hipStream_t stream, const RawQuery* raw) {
+                  float* lse_part, hipStream_t stream, const RawQuery* raw,
+                  const FusedStep* step) {
   P2Args a;
+  a.k_new = step ? step->k_new : nullptr;
+  a.v_new = step ? step->v_new : nullptr;
+  a.ks_w = step ? step->k_self : nullptr;
+  a.vs_w = step ? step->v_self : nullptr;
   a.q = q_rot;
   a.q_raw = raw ? raw->q : nullptr;
   a.q_pos0 = raw ? raw->pos0 : 0;
@@ -1154,11 +1223,14 @@ int launch_phase2(const Phase2Geometry& g, const uint16_t* q_rot, const uint16_t
   const int64_t grid = (int64_t)g.batch * g.n_kv_heads * g.n_row_groups * g.n_parts;
   const bool ksplit = phase2_decode_form(g);
   if (raw && (!ksplit || g.q_len > QTab<128>::MAX_TOK)) return -1;
+  if (step && !raw) return -1;
   if (g.head_dim == 128) {
-    if (ksplit) hipLaunchKernelGGL((phase2_kernel<128, true>), dim3(grid), dim3(NTHR), 0, stream, a);
+    if (step) hipLaunchKernelGGL((phase2_kernel<128, true, true>), dim3(grid), dim3(NTHR), 0, stream, a);
+    else if (ksplit) hipLaunchKernelGGL((phase2_kernel<128, true>), dim3(grid), dim3(NTHR), 0, stream, a);
     else hipLaunchKernelGGL((phase2_kernel<128, false>), dim3(grid), dim3(NTHR), 0, stream, a);
   } else {
-    if (ksplit) hipLaunchKernelGGL((phase2_kernel<64, true>), dim3(grid), dim3(NTHR), 0, stream, a);
+    if (step) hipLaunchKernelGGL((phase2_kernel<64, true, true>), dim3(grid), dim3(NTHR), 0, stream, a);
+    else if (ksplit) hipLaunchKernelGGL((phase2_kernel<64, true>), dim3(grid), dim3(NTHR), 0, stream, a);
     else hipLaunchKernelGGL((phase2_kernel<64, false>), dim3(grid), dim3(NTHR), 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -3;

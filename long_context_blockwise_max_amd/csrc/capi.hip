@@ -526,6 +526,77 @@ int pulsar_phase2_decode(const pulsar_attn* a, int32_t batch, int32_t n_shards,
              : PULSAR_EHIP;
 }
 
+size_t pulsar_decode_step_workspace_bytes(const pulsar_attn* a, int32_t batch, int32_t q_len) {
+  if (check_attn(a) != PULSAR_OK || batch < 1 || q_len < 1) return 0;
+  Phase2Geometry pg = phase2_geometry(batch, 1, 1, q_len, a->n_q_heads, a->n_kv_heads,
+                                      a->head_dim, 1);
+  // the rotated query, for shapes that rotate it outside the attention launch
+  return layout2(pg).k_rot;
+}
+
+int pulsar_decode_step(const pulsar_attn* a, int32_t batch, int32_t n_shards, int32_t shard_len,
+                       const uint16_t* qq, const uint16_t* k_new, const uint16_t* v_new,
+                       int32_t q_len, const uint16_t* k_cache, const uint16_t* v_cache,
+                       uint16_t* k_self_cache, uint16_t* v_self_cache, int32_t cap,
+                       int32_t n_self, int64_t self_pos0, float* o_part, float* lse_part,
+                       int32_t n_parts, float* o, float* lse, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (check_attn(a) != PULSAR_OK) return check_attn(a);
+  if (q_len < 1 || n_self < 0 || (int64_t)n_self + q_len > cap) return PULSAR_EINVAL;
+  const int32_t want = pulsar_phase2_num_parts(a, batch, n_shards, shard_len, q_len, 1);
+  if (want <= 0) return want < 0 ? want : PULSAR_EINVAL;
+  if (n_parts != want || cap < 8 || self_pos0 < 0) return PULSAR_EINVAL;
+  if (cap % 8 != 0) return PULSAR_EUNSUPPORTED;
+  if (!aligned16(qq) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(o_part) ||
+      !lse_part || !aligned16(k_self_cache) || !aligned16(v_self_cache) || !aligned16(o))
+    return PULSAR_EINVAL;
+  if (n_shards > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) return PULSAR_EINVAL;
+  if (n_shards > 0 && shard_len % 8 != 0) return PULSAR_EUNSUPPORTED;
+  if ((int64_t)batch * n_shards * shard_len * a->n_kv_heads > INT32_MAX) return PULSAR_EUNSUPPORTED;
+  if ((int64_t)batch * q_len > INT32_MAX / 2) return PULSAR_EUNSUPPORTED;
+  if ((int64_t)q_len * a->n_q_heads > INT32_MAX) return PULSAR_EUNSUPPORTED;
+  const int32_t n_after = n_self + q_len;
+  Phase2Geometry pg = phase2_geometry(batch, n_shards, n_shards > 0 ? shard_len : 1, q_len,
+                                      a->n_q_heads, a->n_kv_heads, a->head_dim, 1);
+  if (!phase2_grid_ok(pg)) return PULSAR_EUNSUPPORTED;
+  if (!ws || ws_bytes < pulsar_decode_step_workspace_bytes(a, batch, q_len)) return PULSAR_EWORKSPACE;
+  if (!aligned16(ws)) return PULSAR_EINVAL;
+  hipStream_t s = as_stream(stream);
+  const int64_t q_pos0 = self_pos0 + n_self;   // the new tokens are the queries
+  SelfShard self{};
+  self.k = k_self_cache;
+  self.v = v_self_cache;
+  self.k_seq = (int64_t)cap * a->n_kv_heads * a->head_dim;
+  self.v_seq = (int64_t)a->n_kv_heads * a->head_dim * cap;
+  self.n = n_after;
+  self.v_ld = cap;
+  if (phase2_decode_form(pg) && q_len <= 32) {
+    // the attention launch appends the new tokens itself, then the merge
+    const RawQuery raw{qq, q_pos0, a->rope_base, a->rope_scaling};
+    const FusedStep step{k_new, v_new, k_self_cache, v_self_cache};
+    if (launch_phase2(pg, nullptr, k_cache, v_cache, self, o_part, lse_part, s, &raw, &step))
+      return PULSAR_EHIP;
+    return launch_merge(batch, n_parts, q_len, a->n_q_heads, a->head_dim, o_part, lse_part, o,
+                        lse, s) == 0
+               ? PULSAR_OK
+               : PULSAR_EHIP;
+  }
+  // other shapes: append, rotate the query, attend, merge
+  if (launch_self_append(k_new, v_new, batch, q_len, n_self, cap, a->n_kv_heads, a->head_dim,
+                         self_pos0, a->rope_base, a->rope_scaling, k_self_cache, v_self_cache, s))
+    return PULSAR_EHIP;
+  uint16_t* q_rot = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + layout2(pg).q_rot);
+  if (launch_phase2_prep(qq, nullptr, nullptr, batch, q_len, a->n_q_heads, a->n_kv_heads,
+                         a->head_dim, q_pos0, a->rope_base, a->rope_scaling, 8, q_rot, nullptr,
+                         nullptr, s))
+    return PULSAR_EHIP;
+  if (launch_phase2(pg, q_rot, k_cache, v_cache, self, o_part, lse_part, s)) return PULSAR_EHIP;
+  return launch_merge(batch, n_parts, q_len, a->n_q_heads, a->head_dim, o_part, lse_part, o, lse,
+                      s) == 0
+             ? PULSAR_OK
+             : PULSAR_EHIP;
+}
+
 int pulsar_lse_merge(int32_t batch, int32_t n_parts, int32_t q_len, int32_t n_q_heads,
                      int32_t head_dim, const float* o_part, const float* lse_part, float* o,
                      float* lse, void* stream) {

@@ -97,11 +97,24 @@ struct RawQuery {
 // one 32-row wave (at most 32 query tokens)
 bool phase2_decode_form(const Phase2Geometry& g);
 
+// The append of a generation step folded into the decode-form launch: the query
+// tokens are the last lq self tokens, and the launch appends them itself before
+// it stages any tile (k_new / v_new [B][lq][Hkv][d] pre-RoPE into the self
+// caches k_self [B][cap][Hkv][d] and d-major v_self [B][Hkv][d][cap]).
+struct FusedStep {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_self;
+  uint16_t* v_self;
+};
+
 // q_rot [B][Lq][Hq][d] already rotated; or raw != nullptr (decode form only):
-// the kernel rotates raw->q [B][Lq][Hq][d] itself and q_rot is not read
+// the kernel rotates raw->q [B][Lq][Hq][d] itself and q_rot is not read.
+// step != nullptr (needs raw): the append above in the same launch.
 int launch_phase2(const Phase2Geometry& g, const uint16_t* q_rot, const uint16_t* k_cache,
                   const uint16_t* v_cache, const SelfShard& self, float* o_part,
-                  float* lse_part, hipStream_t stream, const RawQuery* raw = nullptr);
+                  float* lse_part, hipStream_t stream, const RawQuery* raw = nullptr,
+                  const FusedStep* step = nullptr);
 
 // Append n_new tokens to self caches of capacity cap holding n_self tokens:
 // k_new / v_new [B][n_new][Hkv][d] pre-RoPE, token j at position pos0 + n_self + j;

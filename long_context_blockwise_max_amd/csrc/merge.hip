@@ -1,57 +1,10 @@
-// Exact log-sum-exp merge of partial attention results.
-//
-// "Dropping the Anchor ..." Section 2.2: an online-softmax merge of the
-// gathered per-shard results gives exact attention over all retained shards.
-// The Star Attention review states the corrected update: part h contributes
-// exp(s_h - s_global) * A_h, where A_h is the part's normalised output and s_h
-// its log-sum-exp.  Hence, per query row and head,
-//   lse = ln sum_p exp(lse_p),   o = sum_p exp(lse_p - lse) * o_p.
-// Parts with lse = -inf (no keys) contribute nothing.
-//
-// One wave per (sequence, token, head) row.  The lanes read the parts' LSEs in
-// parallel (lane p takes parts p, p + 64, ...) and reduce max and sum across the
-// wave; the weighted sum of the part outputs then runs over 8 parts at a time
-// with independent loads (lane l owns D/64 adjacent output columns), the
-// weight of each part broadcast from the lane that computed it.  A part with
-// lse = -inf (no keys) is excluded by a select, so whatever its output row
-// holds (0/0 included) never reaches the sum.
-#include <math.h>
-
-#include "common.hpp"
+// Exact log-sum-exp merge of partial attention results: one wave per
+// (sequence, token, head) row, each running merge_row (merge_row.hpp, where the
+// formula and its sources are stated).
 #include "launch.hpp"
+#include "merge_row.hpp"
 
 namespace pulsar {
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-template <int D>
-struct Cols;
-template <>
-struct Cols<128> {
-  typedef float2 T;
-  static __device__ __forceinline__ void fma(float w, T x, T& a) {
-    a.x = fmaf(w, x.x, a.x);
-    a.y = fmaf(w, x.y, a.y);
-  }
-  static __device__ __forceinline__ T zero() { return make_float2(0.f, 0.f); }
-  static __device__ __forceinline__ T scale(T a, float s) { return make_float2(a.x * s, a.y * s); }
-};
-template <>
-struct Cols<64> {
-  typedef float T;
-  static __device__ __forceinline__ void fma(float w, T x, T& a) { a = fmaf(w, x, a); }
-  static __device__ __forceinline__ T zero() { return 0.f; }
-  static __device__ __forceinline__ T scale(T a, float s) { return a * s; }
-};
 
 template <int D>
 __global__ void __launch_bounds__(256) lse_merge_kernel(int64_t n_rows, int32_t n_parts,
@@ -60,54 +13,13 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(int64_t n_rows, int32_t 
                                                         const float* __restrict__ lse_part,
                                                         float* __restrict__ o,
                                                         float* __restrict__ lse) {
-  using C = Cols<D>;
-  using T = typename C::T;
-  const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (row >= n_rows) return;
   const int64_t seq = row / rows_per_seq;
   const int64_t r = row - seq * rows_per_seq;
   const int64_t base = seq * n_parts * (int64_t)rows_per_seq + r;  // row of part 0
-  auto part_row = [&](int p) { return base + (int64_t)p * rows_per_seq; };
-
-  float mx = -INFINITY;
-  for (int p = lane; p < n_parts; p += 64) mx = fmaxf(mx, lse_part[part_row(p)]);
-  mx = wave_max(mx);
-  T acc = C::zero();
-  float sum = 0.f;
-  if (mx > -INFINITY) {
-    for (int p0 = 0; p0 < n_parts; p0 += 64) {
-      const int pl = p0 + lane;
-      const float lp = pl < n_parts ? lse_part[part_row(pl)] : -INFINITY;
-      const float wl = lp > -INFINITY ? expf(lp - mx) : 0.f;
-      sum += wl;
-      const int cnt = min(64, n_parts - p0);
-      int j = 0;
-      for (; j + 8 <= cnt; j += 8) {
-        T x[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          x[u] = reinterpret_cast<const T*>(o_part + part_row(p0 + j + u) * D)[lane];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float w = __shfl(wl, j + u);
-          T y = x[u];
-          if (!(w > 0.f)) y = C::zero();
-          C::fma(w, y, acc);
-        }
-      }
-      for (; j < cnt; ++j) {
-        const float w = __shfl(wl, j);
-        T y = reinterpret_cast<const T*>(o_part + part_row(p0 + j) * D)[lane];
-        if (!(w > 0.f)) y = C::zero();
-        C::fma(w, y, acc);
-      }
-    }
-    sum = wave_sum(sum);
-  }
-  const float inv = sum > 0.f ? 1.f / sum : 0.f;
-  reinterpret_cast<T*>(o + row * D)[lane] = C::scale(acc, inv);
-  if (lse && lane == 0) lse[row] = sum > 0.f ? mx + logf(sum) : -INFINITY;
+  merge_row<D>(o_part, lse_part, base, rows_per_seq, n_parts, o + row * D,
+                      lse ? lse + row : nullptr);
 }
 
 int launch_merge(int32_t batch, int32_t n_parts, int32_t q_len, int32_t n_q_heads,

@@ -186,6 +186,8 @@ class HotPath:
                                dtype=torch.uint8, device=dev)
         self.o1 = torch.empty((g.batch, 1, hq, d), dtype=torch.float32, device=dev)
         self.lse1 = torch.empty((g.batch, 1, hq), dtype=torch.float32, device=dev)
+        self.ws_step = torch.empty(max(B.pulsar_decode_step_workspace_bytes(self.cattn, g.batch, 1), 256),
+                                   dtype=torch.uint8, device=dev)
         self.self_append(self.k_self, self.v_self, g.q_len)
 
     def self_append(self, k_new, v_new, n_new, stream=None):
@@ -194,22 +196,34 @@ class HotPath:
                              k_new, v_new, self.k_self_cache, self.v_self_cache, stream)
         self.n_self += n_new
 
-    def decode_step(self, q_new=None, k_new=None, v_new=None, o_out=None, stream=None):
+    def decode_step(self, q_new=None, k_new=None, v_new=None, o_out=None, stream=None,
+                    fused=True):
         """One generated token: append its key / value (default k1, v1), attend its
         query (default q1) to every retained shard and the self cache, merge into
         o_out (default o1, with its LSE in lse1).  Token tensors are [B][1][H][d]
-        bf16 on the device."""
+        bf16 on the device.  fused: one pulsar_decode_step call; otherwise
+        pulsar_self_append, pulsar_phase2_decode and pulsar_lse_merge."""
         g = self.geo
         q_new = self.q1 if q_new is None else q_new
-        self.self_append(self.k1 if k_new is None else k_new, self.v1 if v_new is None else v_new,
-                         1, stream)
+        k_new = self.k1 if k_new is None else k_new
+        v_new = self.v1 if v_new is None else v_new
+        o = self.o1 if o_out is None else o_out
+        lse = self.lse1 if o_out is None else None
+        if fused:
+            B.pulsar_decode_step(self.cattn, g.batch, g.n_blocks, g.block_size, q_new, k_new, v_new,
+                                 1, self.k_cache, self.v_cache, self.k_self_cache,
+                                 self.v_self_cache, self.cap, self.n_self, g.context_len,
+                                 self.o_part1, self.lse_part1, self.n_parts1, o, lse, self.ws_step,
+                                 stream)
+            self.n_self += 1
+            return
+        self.self_append(k_new, v_new, 1, stream)
         B.pulsar_phase2_decode(self.cattn, g.batch, g.n_blocks, g.block_size, q_new, 1,
                                self.k_cache, self.v_cache, self.k_self_cache, self.v_self_cache,
                                self.cap, self.n_self, g.context_len, self.o_part1, self.lse_part1,
                                self.n_parts1, self.ws1, stream)
         B.pulsar_lse_merge(g.batch, self.n_parts1, 1, g.n_q_heads, g.head_dim, self.o_part1,
-                           self.lse_part1, self.o1 if o_out is None else o_out,
-                           self.lse1 if o_out is None else None, stream)
+                           self.lse_part1, o, lse, stream)
 
     def capture_generation(self, q_new, k_new, v_new):
         """Capture n generation steps (self cache primed anew, then one step per

@@ -264,3 +264,24 @@ def test_noalloc_query_rejects_on_the_host():
     assert q2(1, 64, n, pos0=-1) == B.PULSAR_EINVAL
     assert lib.pulsar_phase2_query_noalloc(A, 1, 8, 16384, FAKE, 64, 0, FAKE, FAKE, FAKE, None,
                                            FAKE, FAKE, n, None) == B.PULSAR_EINVAL
+
+
+@needs_lib
+def test_decode_step_rejects_on_the_host():
+    lib = B.lib()
+    A = ctypes.byref(ATTN)
+    n = B.pulsar_phase2_num_parts(ATTN, 1, 8, 16384, 1, True)
+    ws = B.pulsar_decode_step_workspace_bytes(ATTN, 1, 1)
+    assert ws >= 32 * 128 * 2                              # one rotated query token
+
+    def step(q_len=1, cap=128, n_self=64, n_parts=n, wsb=ws, pos0=131072, ptr=FAKE):
+        return lib.pulsar_decode_step(A, 1, 8, 16384, FAKE, ptr, FAKE, q_len, FAKE, FAKE, FAKE, FAKE,
+                                      cap, n_self, pos0, FAKE, FAKE, n_parts, FAKE, None, FAKE, wsb,
+                                      None)
+
+    assert step(n_parts=n + 1) == B.PULSAR_EINVAL
+    assert step(n_self=128) == B.PULSAR_EINVAL            # no room for the new token
+    assert step(cap=124, n_self=64) == B.PULSAR_EUNSUPPORTED
+    assert step(wsb=ws - 1) == B.PULSAR_EWORKSPACE
+    assert step(pos0=-1) == B.PULSAR_EINVAL
+    assert step(ptr=FAKE_MIS) == B.PULSAR_EINVAL

@@ -136,3 +136,95 @@ def test_generation_at_128k_matches_the_oracle():
         assert_close(path.o1.cpu().numpy()[0], want_o, f"128k decode step {step} O")
         assert_close(path.lse1.cpu().numpy()[0], want_lse, f"128k decode step {step} LSE",
                      max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+def _three_calls(path, B, q, k, v, q_len, o, lse):
+    """The generation step as pulsar_self_append + pulsar_phase2_decode + pulsar_lse_merge."""
+    import torch
+    g = path.geo
+    n_parts = B.pulsar_phase2_num_parts(path.cattn, g.batch, g.n_blocks, g.block_size, q_len, True)
+    o_part = torch.empty((g.batch, n_parts, q_len, g.n_q_heads, g.head_dim), device="cuda")
+    lse_part = torch.empty((g.batch, n_parts, q_len, g.n_q_heads), device="cuda")
+    ws = torch.empty(max(B.pulsar_phase2_workspace_bytes(path.cattn, g.batch, q_len, False), 256),
+                     dtype=torch.uint8, device="cuda")
+    B.pulsar_self_append(path.cattn, g.batch, path.cap, path.n_self, q_len, g.context_len, k, v,
+                         path.k_self_cache, path.v_self_cache)
+    B.pulsar_phase2_decode(path.cattn, g.batch, g.n_blocks, g.block_size, q, q_len, path.k_cache,
+                           path.v_cache, path.k_self_cache, path.v_self_cache, path.cap,
+                           path.n_self + q_len, g.context_len, o_part, lse_part, n_parts, ws)
+    B.pulsar_lse_merge(g.batch, n_parts, q_len, g.n_q_heads, g.head_dim, o_part, lse_part, o, lse)
+
+
+def _one_call(path, B, q, k, v, q_len, o, lse, ws):
+    import torch
+    g = path.geo
+    n_parts = B.pulsar_phase2_num_parts(path.cattn, g.batch, g.n_blocks, g.block_size, q_len, True)
+    o_part = torch.full((g.batch, n_parts, q_len, g.n_q_heads, g.head_dim), float("nan"), device="cuda")
+    lse_part = torch.full((g.batch, n_parts, q_len, g.n_q_heads), float("nan"), device="cuda")
+    B.pulsar_decode_step(path.cattn, g.batch, g.n_blocks, g.block_size, q, k, v, q_len, path.k_cache,
+                         path.v_cache, path.k_self_cache, path.v_self_cache, path.cap, path.n_self,
+                         g.context_len, o_part, lse_part, n_parts, o, lse, ws)
+
+
+STEP_CASES = {
+    # name: (workload overrides, tokens per step, steps)
+    "tiny_1": ({}, 1, 3),
+    "batch3_1": (CASES["decode_batch"], 1, 4),
+    "long_1": (CASES["long_gen"], 1, 22),
+    "self_heavy_1": (CASES["self_heavy_d128"], 1, 3),
+    "llama3_1": (CASES["llama3"], 1, 2),
+    # several tokens a step, still appended by the attention launch (4 heads x 5
+    # tokens in one wave);
+    # the new tokens can straddle a 64-token tile
+    "g4_5tok": (dict(CASES["g4_d128"], q_len=62), 5, 3),
+    # 8 heads x 5 tokens do not fit one wave: the three calls run inside
+    "g8_5tok": (dict(n_blocks=2, block_size=256, n_q_heads=8, n_kv_heads=1, head_dim=128, q_len=3,
+                     budget_chunks=1, n_planted=0), 5, 2),
+}
+
+
+@pytest.mark.parametrize("name", list(STEP_CASES))
+def test_one_call_step_equals_the_three_calls(name):
+    """pulsar_decode_step against pulsar_self_append + pulsar_phase2_decode +
+    pulsar_lse_merge on the same inputs: the merged outputs and LSEs of every step
+    and the self caches afterwards are bit-identical (for one-token steps the
+    attention launch appends the new tokens itself)."""
+    torch = torch_cuda()
+    from long_context_blockwise_max_amd import binding as B
+    over, q_len, n_steps = STEP_CASES[name]
+    w = W.with_(W.WORKLOADS["tiny"], name=name, **over)
+    rng = np.random.default_rng(7)
+    bf = lambda shape: torch.from_numpy(W.f32_to_bf16_bits(
+        rng.standard_normal(shape, dtype=np.float32)).view(np.int16)).view(torch.bfloat16).to("cuda")
+    fused, plain = Case(w), Case(w)
+    fused.run()
+    plain.run()
+    fused.path.decode_setup(q_len * n_steps)
+    plain.path.decode_setup(q_len * n_steps)
+    g = fused.path.geo
+    ws = torch.empty(max(B.pulsar_decode_step_workspace_bytes(fused.path.cattn, g.batch, q_len), 256),
+                     dtype=torch.uint8, device="cuda")
+    for step in range(n_steps):
+        q = bf((g.batch, q_len, g.n_q_heads, g.head_dim))
+        k = bf((g.batch, q_len, g.n_kv_heads, g.head_dim))
+        v = bf((g.batch, q_len, g.n_kv_heads, g.head_dim))
+        outs = []
+        for case, fn in ((fused, _one_call), (plain, _three_calls)):
+            o = torch.full((g.batch, q_len, g.n_q_heads, g.head_dim), float("nan"), device="cuda")
+            lse = torch.full((g.batch, q_len, g.n_q_heads), float("nan"), device="cuda")
+            if fn is _one_call:
+                fn(case.path, B, q, k, v, q_len, o, lse, ws)
+            else:
+                fn(case.path, B, q, k, v, q_len, o, lse)
+            case.path.n_self += q_len
+            outs.append((o, lse))
+        torch.cuda.synchronize()
+        (o_a, l_a), (o_b, l_b) = outs
+        assert not torch.isnan(o_a).any() and not torch.isnan(l_a).any()
+        assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b), f"{name} step {step}"
+        log(f"[decode-step] {name} step {step}: one call == three calls (self tokens "
+            f"{fused.path.n_self})")
+    n = fused.path.n_self
+    pad = (n + 7) // 8 * 8
+    assert torch.equal(fused.path.k_self_cache[:, :n], plain.path.k_self_cache[:, :n])
+    assert torch.equal(fused.path.v_self_cache[..., :pad], plain.path.v_self_cache[..., :pad])
