@@ -1007,8 +1007,42 @@ phase2_kernel(P2Args a) {
   FlashState<D, NQ> st;
   flash_init(st);
 
-  // keys past the source read the tile's first key (masked below)
+  // Shard tiles are staged through buffer resources over the (sequence, shard,
+  // KV head) slabs: a lane's source offset within a tile is a constant of the
+  // lane (computed here once) and the tile adds a scalar offset, so staging a
+  // tile costs no per-lane address arithmetic.  Keys past the shard read zero
+  // (past the K slab) or the next value row (inside the V slab), both finite
+  // and masked below.  Self tiles (at most a couple per part) take the per-lane
+  // path further down, whose keys past the self tokens read the tile's first key.
+  uint32_t k_vo[KTile<D>::NI], v_vo[VTile<D>::NI];
+  {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int x = 0; x < KTile<D>::NI; ++x) {
+      const int row = staged_k_row<D>(x);
+      const int c = (lane % KTile<D>::CPR) ^ KTile<D>::sw(row);
+      k_vo[x] = (uint32_t)((row * D + 8 * c) * 2);
+    }
+#pragma unroll
+    for (int y = 0; y < VTile<D>::NI; ++y)
+      v_vo[y] = (uint32_t)((staged_v_d<D>(y) * (uint32_t)a.n + 8 * staged_v_chunk<D>(y)) * 2);
+  }
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   auto stage_part_tile = [&](char* dst, const Cur& c) __attribute__((always_inline)) {
+    if (c.shard < a.n_shards) {
+      const int64_t base = (((int64_t)bb * a.n_shards + c.shard) * a.hkv + g) * a.n * D;
+      const uint32_t bytes = (uint32_t)a.n * D * 2;
+      const __amdgpu_buffer_rsrc_t krs = raw_rsrc(a.kc + base, bytes);
+      const __amdgpu_buffer_rsrc_t vrs = raw_rsrc(a.vc + base, bytes);
+      const uint32_t lo = (uint32_t)c.lt * KT;
+#pragma unroll
+      for (int x = 0; x < KTile<D>::NI; ++x)
+        dma16_buf(krs, k_vo[x], lo * D * 2, dst + (wv * KTile<D>::NI + x) * 1024);
+#pragma unroll
+      for (int y = 0; y < VTile<D>::NI; ++y)
+        dma16_buf(vrs, v_vo[y], lo * 2, dst + KTile<D>::BYTES + (wv * VTile<D>::NI + y) * 1024);
+      return;
+    }
     const Src r = src_of(c);
     TileSrc<D> sr;
 #pragma unroll

@@ -275,6 +275,7 @@ int phase2_query_checked(const pulsar_attn* a, int32_t batch, int32_t n_shards,
   if (n_shards > 0 && shard_len % 8 != 0) return PULSAR_EUNSUPPORTED;  // d-major value runs of 8
   if (q_pos0 < 0) return PULSAR_EINVAL;
   if ((int64_t)batch * n_shards * shard_len * a->n_kv_heads > INT32_MAX) return PULSAR_EUNSUPPORTED;
+  if ((int64_t)shard_len * a->head_dim * 2 > UINT32_MAX) return PULSAR_EUNSUPPORTED;  // slab bytes
   if ((int64_t)batch * q_len > INT32_MAX / 2) return PULSAR_EUNSUPPORTED;
   *out = phase2_geometry(batch, n_shards, n_shards > 0 ? shard_len : 1, q_len, a->n_q_heads,
                          a->n_kv_heads, a->head_dim, has_self);
@@ -493,6 +494,7 @@ int pulsar_phase2_decode(const pulsar_attn* a, int32_t batch, int32_t n_shards,
   if (n_shards > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) return PULSAR_EINVAL;
   if (n_shards > 0 && shard_len % 8 != 0) return PULSAR_EUNSUPPORTED;
   if ((int64_t)batch * n_shards * shard_len * a->n_kv_heads > INT32_MAX) return PULSAR_EUNSUPPORTED;
+  if ((int64_t)shard_len * a->head_dim * 2 > UINT32_MAX) return PULSAR_EUNSUPPORTED;  // slab bytes
   if ((int64_t)batch * q_len > INT32_MAX / 2) return PULSAR_EUNSUPPORTED;
   Phase2Geometry pg = phase2_geometry(batch, n_shards, n_shards > 0 ? shard_len : 1, q_len,
                                       a->n_q_heads, a->n_kv_heads, a->head_dim, 1);
@@ -553,6 +555,7 @@ int pulsar_decode_step(const pulsar_attn* a, int32_t batch, int32_t n_shards, in
   if (n_shards > 0 && (!aligned16(k_cache) || !aligned16(v_cache))) return PULSAR_EINVAL;
   if (n_shards > 0 && shard_len % 8 != 0) return PULSAR_EUNSUPPORTED;
   if ((int64_t)batch * n_shards * shard_len * a->n_kv_heads > INT32_MAX) return PULSAR_EUNSUPPORTED;
+  if ((int64_t)shard_len * a->head_dim * 2 > UINT32_MAX) return PULSAR_EUNSUPPORTED;  // slab bytes
   if ((int64_t)batch * q_len > INT32_MAX / 2) return PULSAR_EUNSUPPORTED;
   if ((int64_t)q_len * a->n_q_heads > INT32_MAX) return PULSAR_EUNSUPPORTED;
   const int32_t n_after = n_self + q_len;
