@@ -122,9 +122,10 @@ constexpr float kRescaleSlack = 8.f;
 constexpr float kRescaleBound = 256.f;   // 2^kRescaleSlack
 
 // p = exp2(s * sl2 - m) for the 16 scores of one accumulator, rounded to bf16
-// into the two PV operands; sum = the fp32 sum of the p.  (v_dot2_f32_bf16 would
-// add two rounded p per instruction, but interleaved with the MFMAs of this
-// loop it produced wrong sums, so plain adds are used.)
+// into the two PV operands; sum = the fp32 sum of the p.  (Summing the rounded
+// pairs with v_dot2_f32_bf16, eight instructions instead of sixteen adds, gives
+// correct sums but a 3 % slower loop: the dot products into one accumulator
+// form a longer dependent chain.)
 template <int NQ>
 __device__ __forceinline__ void softmax_p(const f32x16& s, float sl2, float m, bf16x8 (&p)[2],
                                           float& sum) {
