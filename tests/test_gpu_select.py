@@ -126,17 +126,19 @@ def test_select_chunk_sizes(chunk):
     assert status == 0
 
 
-def test_select_without_chunk_scores_out():
-    """chunk_min_df = NULL: the scores go through the workspace; same selection."""
+@pytest.mark.parametrize("n_blocks", [5, 8])
+def test_select_without_chunk_scores_out(n_blocks):
+    """chunk_min_df = NULL and df = NULL: the scores and df go through the
+    workspace; same selection."""
     torch = torch_cuda()
     from long_context_blockwise_max_amd import binding as B
-    tok = W.small_vocab_tokens(3, 5, 1024, 64)
-    g = B.make_geom(5, 1024, 32, 6, 64, 64)
+    tok = W.small_vocab_tokens(3, n_blocks, 1024, 64)
+    g = B.make_geom(n_blocks, 1024, 32, 6, 64, 64)
     dev = torch.device("cuda")
     t = torch.from_numpy(np.ascontiguousarray(tok, dtype=np.int32)).to(dev)
-    sel = torch.full((5, 6), -7, dtype=torch.int32, device=dev)
+    sel = torch.full((n_blocks, 6), -7, dtype=torch.int32, device=dev)
     ws = torch.full((B.pulsar_workspace_bytes(g, None),), 0xAB, dtype=torch.uint8, device=dev)
     B.pulsar_select(g, t, sel, None, None, ws)
     torch.cuda.synchronize()
-    want_sel, _, _ = OS.select(tok, 5, 1024, 32, 6, 64)
+    want_sel, _, _ = OS.select(tok, n_blocks, 1024, 32, 6, 64)
     np.testing.assert_array_equal(sel.cpu().numpy(), want_sel)
