@@ -37,9 +37,80 @@ def parse():
                     help="Phase-1 rows of the last block the oracle recomputes on the host")
     ap.add_argument("--gen-tokens", type=int, default=128,
                     help="generated tokens timed after the main steps (0: none)")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the power and clock reading (a 2 s Phase-1 burst after the timed steps)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (counter calibration)")
     return ap.parse_args()
+
+
+class PowerSampler:
+    """Socket power and gfx clock of the GPU from the AMD SMI library, polled every
+    10 ms on a thread (best effort: an empty record where the library or the
+    reading is unavailable).  The clock is the median over the XCDs' current gfx
+    clocks.  The metrics table trails the load by a few hundred milliseconds, so
+    only samples after the first `settle_s` seconds of a run are summarised."""
+
+    def __init__(self):
+        self.smi = self.h = None
+        self.samples = []
+        self.cap_w = self.idle_w = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.smi = amdsmi
+            self.h = amdsmi.amdsmi_get_processor_handles()[0]
+            cap = amdsmi.amdsmi_get_power_cap_info(self.h).get("power_cap")
+            self.cap_w = cap / 1e6 if isinstance(cap, (int, float)) else None
+            self.idle_w = self._read()[0]
+        except Exception:
+            self.h = None
+
+    def _read(self):
+        m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+        pw = m.get("current_socket_power")
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and 0 < c < 65535]
+        return (pw if isinstance(pw, (int, float)) else None,
+                sorted(clks)[len(clks) // 2] if clks else None)
+
+    def run(self, fn, seconds=2.0, settle_s=1.0):
+        """Call fn() back to back for `seconds` while sampling; the summary of the
+        samples taken after `settle_s`."""
+        import threading
+        import torch
+        if self.h is None:
+            return {}
+        samples, stop = [], threading.Event()
+        t0 = time.perf_counter()
+
+        def loop():
+            while not stop.is_set():
+                try:
+                    samples.append((time.perf_counter() - t0,) + self._read())
+                except Exception:
+                    pass
+                time.sleep(0.01)
+
+        th = threading.Thread(target=loop, daemon=True)
+        th.start()
+        calls = 0
+        while time.perf_counter() - t0 < seconds:
+            fn()
+            calls += 1
+            torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        late = [x for x in samples if x[0] >= settle_s]
+        pw = sorted(x[1] for x in late if x[1] is not None)
+        ck = sorted(x[2] for x in late if x[2] is not None)
+        return {"source": "AMD SMI gpu metrics, polled every 10 ms",
+                "load": f"pulsar_phase1_attend back to back for {seconds} s ({calls} calls), "
+                        f"samples after the first {settle_s} s",
+                "cap_w": self.cap_w, "idle_w": self.idle_w,
+                "socket_w_median": pw[len(pw) // 2] if pw else None,
+                "socket_w_max": pw[-1] if pw else None,
+                "gfxclk_mhz_median": ck[len(ck) // 2] if ck else None,
+                "samples": len(late)}
 
 
 def recorded_traffic(workload, kernel):
@@ -354,6 +425,7 @@ def main():
              lambda: torch.sum(flush, dim=0, out=flush_sink), path.phase2, path.merge)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
           for _ in range(args.steps)]
+    power = PowerSampler()   # the idle reading comes before the timed steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -431,6 +503,7 @@ def main():
                             "unit": "GB/s", "frac": round(p2_gbs / PEAK_HBM_GBS, 4),
                             "traffic": recorded_traffic(w.name, "phase2_kernel")},
     }
+    out["power"] = {} if args.no_power else power.run(path.phase1_attend)
     out["prefix_rows"] = prefix_rows(path, w, stream)
     out["selection_methods"] = selection_methods(path, w, stream)
     if args.gen_tokens > 0:
