@@ -22,7 +22,8 @@
 // rescale of O touches only the lane's own registers.
 //
 // Tiles are staged with direct global->LDS loads (buffer_load_dwordx4 ... lds in
-// Phase 1, global_load_lds_dwordx4 in Phase 2), one barrier per tile: two slots,
+// Phase 1 and for Phase-2 shard tiles, global_load_lds_dwordx4 for the Phase-2
+// self tiles), one barrier per tile: two slots,
 // one tile ahead, for Phase 1 and the Phase-2 query; four slots, three tiles
 // ahead, for the Phase-2 decode form, which streams from HBM with little work
 // per tile.  The 16-byte chunks of every LDS row are XOR-swizzled so that
