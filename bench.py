@@ -49,7 +49,10 @@ class PowerSampler:
     10 ms on a thread (best effort: an empty record where the library or the
     reading is unavailable).  The clock is the median over the XCDs' current gfx
     clocks.  The metrics table trails the load by a few hundred milliseconds, so
-    only samples after the first `settle_s` seconds of a run are summarised."""
+    only samples after the first `settle_s` seconds of a run are summarised.  The
+    firmware also counts, per sample of its own (1 kHz), whether the chip was held
+    at its package power limit or at a thermal limit; the share of those samples
+    over the same window is reported."""
 
     def __init__(self):
         self.smi = self.h = None
@@ -65,6 +68,27 @@ class PowerSampler:
             self.idle_w = self._read()[0]
         except Exception:
             self.h = None
+
+    RESIDENCY = {"power_limit": ("ppt_residency_acc",),
+                 "thermal_limit": ("socket_thm_residency_acc", "vr_thm_residency_acc",
+                                   "hbm_thm_residency_acc")}
+
+    def _counters(self):
+        m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+        keys = ("accumulation_counter",) + sum(self.RESIDENCY.values(), ())
+        return {k: m.get(k) for k in keys}
+
+    def _residency(self, c0, c1):
+        def delta(k):
+            a, b = c0.get(k), c1.get(k)
+            return b - a if isinstance(a, int) and isinstance(b, int) else None
+        n = delta("accumulation_counter")
+        out = {}
+        for name, keys in self.RESIDENCY.items():
+            d = [delta(k) for k in keys]
+            out[f"{name}_share"] = (round(sum(d) / n, 4) if n and all(x is not None for x in d)
+                                    else None)
+        return out
 
     def _read(self):
         m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
@@ -94,10 +118,14 @@ class PowerSampler:
         th = threading.Thread(target=loop, daemon=True)
         th.start()
         calls = 0
+        c0 = None
         while time.perf_counter() - t0 < seconds:
+            if c0 is None and time.perf_counter() - t0 >= settle_s:
+                c0 = self._counters()
             fn()
             calls += 1
             torch.cuda.synchronize()
+        c1 = self._counters()
         stop.set()
         th.join()
         late = [x for x in samples if x[0] >= settle_s]
@@ -110,7 +138,8 @@ class PowerSampler:
                 "socket_w_median": pw[len(pw) // 2] if pw else None,
                 "socket_w_max": pw[-1] if pw else None,
                 "gfxclk_mhz_median": ck[len(ck) // 2] if ck else None,
-                "samples": len(late)}
+                "samples": len(late),
+                **(self._residency(c0, c1) if c0 is not None else {})}
 
 
 def recorded_traffic(workload, kernel):
