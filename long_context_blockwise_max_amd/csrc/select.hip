@@ -130,13 +130,21 @@ __global__ void __launch_bounds__(kDfThreads) select_bits(const int32_t* __restr
   for (int w = threadIdx.x; w < nwords; w += blockDim.x) out[w] = bits[w];
 }
 
-// number of blocks whose bitmap holds id
+// number of blocks whose bitmap holds id, 8 bitmaps a round with every read of
+// the round issued before the first count (a round past the last block re-reads
+// block 0's word and counts nothing for it)
 __device__ __forceinline__ int df_of(const uint32_t* __restrict__ bits, int nwords, int n_blocks,
                                      int32_t id) {
   const uint32_t* b = bits + (id >> 5);
   const int sh = id & 31;
   int c = 0;
-  for (int j = 0; j < n_blocks; ++j) c += (b[(int64_t)j * nwords] >> sh) & 1;
+  for (int j0 = 0; j0 < n_blocks; j0 += 8) {
+    uint32_t w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = b[(int64_t)(j0 + u < n_blocks ? j0 + u : 0) * nwords];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c += j0 + u < n_blocks ? (w[u] >> sh) & 1 : 0;
+  }
   return c;
 }
 
