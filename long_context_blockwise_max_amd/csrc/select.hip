@@ -364,21 +364,42 @@ __global__ void __launch_bounds__(256) select_keys(
       key_mul(k, f);
     }
     if (bad) atomicOr(status, 1);
+  } else if (METHOD == 1) {
+    // 8 tokens at a time: their ids, then their df values, each group of loads in
+    // flight together (chunk_size is a multiple of 8); the product in token order
+    const int j = (int)(idx / n_chunks), c = (int)(idx % n_chunks);
+    const int32_t* ct = tok + (int64_t)j * block_size + (int64_t)c * chunk_size;
+    bool bad = false;
+    for (int e0 = 0; e0 < chunk_size; e0 += 8) {
+      const u32x4 x0 = reinterpret_cast<const u32x4*>(ct + e0)[0];
+      const u32x4 x1 = reinterpret_cast<const u32x4*>(ct + e0)[1];
+      int32_t ids[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ids[e] = (int32_t)x0[e];
+        ids[4 + e] = (int32_t)x1[e];
+      }
+      uint32_t f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool in_range = ids[e] >= 0 && ids[e] < vocab;
+        bad |= !in_range;
+        f[e] = (uint32_t)df[in_range ? ids[e] : 0];
+        if (!in_range) f[e] = (uint32_t)n_blocks;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) key_mul(k, f[e]);
+    }
+    if (bad) atomicOr(status, 1);
   } else {
     const int j = (int)(idx / n_chunks), c = (int)(idx % n_chunks);
     const int32_t* ct = tok + (int64_t)j * block_size + (int64_t)c * chunk_size;
     bool bad = false;
     for (int e = 0; e < chunk_size; ++e) {
       const int32_t id = ct[e];
-      const bool in_range = id >= 0 && id < vocab;
-      bad |= !in_range;
-      uint32_t f;
-      if constexpr (METHOD == 1) {
-        f = in_range ? (uint32_t)df[id] : (uint32_t)n_blocks;
-      } else {
-        f = 0;
-        for (int e2 = 0; e2 < chunk_size; ++e2) f += ct[e2] == id;
-      }
+      bad |= !(id >= 0 && id < vocab);
+      uint32_t f = 0;
+      for (int e2 = 0; e2 < chunk_size; ++e2) f += ct[e2] == id;
       key_mul(k, f);
     }
     if (bad) atomicOr(status, 1);
