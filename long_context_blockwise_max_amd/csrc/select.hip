@@ -411,19 +411,27 @@ __global__ void __launch_bounds__(256) select_keys(
 }
 
 // -1, 0, 1 as key a (registers) is smaller than, equal to or larger than key b
+// -1, 0 or 1 as key a is below, equal to or above key b (16-byte aligned).  All
+// limbs are read at once and compared without branches, so that the reads of
+// successive comparisons are not serialised behind each other's outcomes.
 __device__ __forceinline__ int key_cmp(const uint32_t (&a)[kKeyLimbs], const uint32_t* b) {
+  static_assert(kKeyLimbs == 8, "two 16-byte reads per key");
+  const u32x4 b0 = reinterpret_cast<const u32x4*>(b)[0];
+  const u32x4 b1 = reinterpret_cast<const u32x4*>(b)[1];
+  const uint32_t y[kKeyLimbs] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  int r = 0;
 #pragma unroll
   for (int i = kKeyLimbs - 1; i >= 0; --i) {
-    const uint32_t y = b[i];
-    if (a[i] != y) return a[i] < y ? -1 : 1;
+    const int c = (int)(a[i] > y[i]) - (int)(a[i] < y[i]);
+    r = r != 0 ? r : c;
   }
-  return 0;
+  return r;
 }
 
 __global__ void __launch_bounds__(kRankTile) select_rank(const uint32_t* __restrict__ keys,
                                                          int32_t n_chunks, int32_t tiles,
                                                          int32_t* __restrict__ ranks) {
-  __shared__ uint32_t other[kRankTile * kKeyLimbs];
+  __shared__ __attribute__((aligned(16))) uint32_t other[kRankTile * kKeyLimbs];
   const int per_block = tiles * tiles;
   const int j = blockIdx.x / per_block;
   const int r = blockIdx.x % per_block;
