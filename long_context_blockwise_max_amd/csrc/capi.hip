@@ -200,8 +200,9 @@ int pulsar_select_method(const pulsar_geom* g, int32_t method, uint64_t seed, co
   int32_t* dfp = reinterpret_cast<int32_t*>(w + l.df);
   uint32_t* keys = reinterpret_cast<uint32_t*>(w + l.keys);
   int32_t* ranks = reinterpret_cast<int32_t*>(w + l.ranks);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(w + l.bits);
   return launch_select_method(method, seed, tok, g->n_blocks, g->block_size, g->chunk_size, kept,
-                              g->vocab_size, sel, dfp, keys, ranks, status,
+                              g->vocab_size, sel, dfp, bits, keys, ranks, status,
                               as_stream(stream)) == 0
              ? PULSAR_OK
              : PULSAR_EHIP;

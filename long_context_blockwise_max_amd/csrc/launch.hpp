@@ -14,12 +14,13 @@ int launch_select(const int32_t* tok, int32_t n_blocks, int32_t block_size, int3
                   uint32_t* bits, int32_t* status, hipStream_t stream);
 
 // method 1 mean IDF, 2 entropy, 3 uniform (seeded), 4 evenly spaced.  Scratch:
-// df [vocab] (mean IDF), keys [N][n_chunks][8] (16-byte aligned), ranks
-// [N][n_chunks]; status[0] is cleared and flags out-of-range ids
+// df [vocab] and bits [N][ceil(V / 32)] words (mean IDF), keys [N][n_chunks][8]
+// (16-byte aligned), ranks [N][n_chunks]; status[0] is cleared and flags
+// out-of-range ids
 int launch_select_method(int32_t method, uint64_t seed, const int32_t* tok, int32_t n_blocks,
                          int32_t block_size, int32_t chunk_size, int32_t kept, int32_t vocab,
-                         int32_t* sel, int32_t* df, uint32_t* keys, int32_t* ranks,
-                         int32_t* status, hipStream_t stream);
+                         int32_t* sel, int32_t* df, uint32_t* bits, uint32_t* keys,
+                         int32_t* ranks, int32_t* status, hipStream_t stream);
 
 int launch_rope_fill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t L,
                      int32_t block_size, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,

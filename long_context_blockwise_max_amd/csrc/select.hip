@@ -19,7 +19,7 @@
 //                   LDS histogram over the score range finds the cut-off score,
 //                   and wave ballots + mbcnt rank ties in chunk order and
 //                   compact the kept chunks in ascending order
-// (The mean-IDF method below counts df with select_clear and select_df instead.)
+// (The mean-IDF method below counts df with the same two kernels.)
 #include <algorithm>
 
 #include "common.hpp"
@@ -30,51 +30,12 @@ namespace pulsar {
 constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / kWave;
 
-__global__ void __launch_bounds__(256) select_clear(int32_t* __restrict__ df, int32_t vocab,
-                                                    int32_t* __restrict__ status) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i == 0) status[0] = 0;
-  for (; i < vocab; i += (int64_t)gridDim.x * blockDim.x) df[i] = 0;
+__global__ void __launch_bounds__(64) select_clear(int32_t* __restrict__ status) {
+  if (threadIdx.x == 0) status[0] = 0;
 }
 
 constexpr int kDfThreads = 1024;
 constexpr int kDfBatch = 16;   // tokens a thread loads before its bitmap updates
-
-__global__ void __launch_bounds__(kDfThreads) select_df(const int32_t* __restrict__ tok,
-                                                        int32_t block_size, int32_t vocab,
-                                                        int32_t* __restrict__ df,
-                                                        int32_t* __restrict__ status) {
-  extern __shared__ uint32_t bits[];  // ceil(vocab / 32) words
-  const int nwords = (vocab + 31) >> 5;
-  for (int w = threadIdx.x; w < nwords; w += blockDim.x) bits[w] = 0u;
-  __syncthreads();
-  const int32_t* t = tok + (int64_t)blockIdx.x * block_size;
-  bool bad = false;
-  // tokens are loaded kDfBatch at a time (independent loads in flight together),
-  // then marked; an id outside [0, V) is skipped and flagged
-  for (int p0 = 0; p0 < block_size; p0 += kDfThreads * kDfBatch) {
-    int32_t ids[kDfBatch];
-#pragma unroll
-    for (int e = 0; e < kDfBatch; ++e) {
-      const int p = p0 + e * kDfThreads + (int)threadIdx.x;
-      ids[e] = p < block_size ? t[p] : -1;
-    }
-#pragma unroll
-    for (int e = 0; e < kDfBatch; ++e) {
-      const int p = p0 + e * kDfThreads + (int)threadIdx.x;
-      const int32_t id = ids[e];
-      if (p >= block_size) continue;
-      if (id < 0 || id >= vocab) {
-        bad = true;
-        continue;
-      }
-      const uint32_t m = 1u << (id & 31);
-      const uint32_t old = atomicOr(&bits[id >> 5], m);
-      if (!(old & m)) atomicAdd(&df[id], 1);
-    }
-  }
-  if (bad) atomicOr(status, 1);
-}
 
 // exclusive prefix of `pred` over the workgroup's threads in thread order;
 // returns this thread's prefix and writes the workgroup total to *total.
@@ -486,28 +447,30 @@ __global__ void __launch_bounds__(256) select_even(int32_t n_blocks, int32_t n_c
 
 int launch_select_method(int32_t method, uint64_t seed, const int32_t* tok, int32_t n_blocks,
                          int32_t block_size, int32_t chunk_size, int32_t kept, int32_t vocab,
-                         int32_t* sel, int32_t* df, uint32_t* keys, int32_t* ranks,
-                         int32_t* status, hipStream_t stream) {
+                         int32_t* sel, int32_t* df, uint32_t* bits, uint32_t* keys,
+                         int32_t* ranks, int32_t* status, hipStream_t stream) {
   const int n_chunks = block_size / chunk_size;
-  // the status word (and df, for mean IDF) start at zero
-  const int32_t clear_n = method == 1 ? vocab : 0;
-  const int clear_blocks = (int)std::min<int64_t>(1024, ((int64_t)clear_n + 255) / 256 + 1);
-  hipLaunchKernelGGL(select_clear, dim3(clear_blocks), dim3(256), 0, stream, df, clear_n, status);
+  if (method == 1 && kept > 0) {
+    // df as Max-IDF counts it: the block bitmaps (whose first workgroup clears the
+    // status word), then the sum over them per id
+    const size_t bitmap_bytes = (size_t)((vocab + 31) / 32) * 4;
+    if (bitmap_bytes > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&select_bits),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bitmap_bytes) != hipSuccess)
+      return -3;
+    hipLaunchKernelGGL(select_bits, dim3(n_blocks), dim3(kDfThreads), bitmap_bytes, stream, tok,
+                       block_size, vocab, bits, status);
+    hipLaunchKernelGGL(select_df_sum, dim3((unsigned)(((int64_t)vocab + 255) / 256)), dim3(256), 0,
+                       stream, bits, n_blocks, vocab, df);
+  } else {
+    hipLaunchKernelGGL(select_clear, dim3(1), dim3(64), 0, stream, status);   // status starts at 0
+  }
   if (kept <= 0) return hipGetLastError() == hipSuccess ? 0 : -3;
   if (method == 4) {
     const int64_t n = (int64_t)n_blocks * kept;
     hipLaunchKernelGGL(select_even, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                        n_blocks, n_chunks, kept, sel);
     return hipGetLastError() == hipSuccess ? 0 : -3;
-  }
-  if (method == 1) {
-    const size_t bitmap_bytes = (size_t)((vocab + 31) / 32) * 4;
-    if (bitmap_bytes > 65536 &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&select_df),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bitmap_bytes) != hipSuccess)
-      return -3;
-    hipLaunchKernelGGL(select_df, dim3(n_blocks), dim3(1024), bitmap_bytes, stream, tok,
-                       block_size, vocab, df, status);
   }
   const int64_t total = (int64_t)n_blocks * n_chunks;
   const dim3 kgrid((unsigned)((total + 255) / 256));
