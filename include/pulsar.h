@@ -131,8 +131,9 @@ int pulsar_select(const pulsar_geom* g, const int32_t* tok, int32_t* sel,
  *   sel   [N][kept] int32 out
  *   seed  UNIFORM only
  *   ws    at least pulsar_workspace_bytes(g, NULL) bytes (it holds 36 bytes of
- *         scratch per chunk for these methods); its first word is the
- *         status word, set to 1 when a token id lies outside [0, vocab_size)
+ *         scratch per chunk for these methods, and for MEAN_IDF the df table and
+ *         the per-block vocabulary bitmaps); its first word is the status word,
+ *         set to 1 when a token id lies outside [0, vocab_size)
  *         (MAX_IDF, MEAN_IDF and ENTROPY read the ids)
  * Errors: PULSAR_EINVAL (also an unknown method), PULSAR_EWORKSPACE,
  * PULSAR_EUNSUPPORTED (mean IDF with N^chunk >= 2^256, entropy with
