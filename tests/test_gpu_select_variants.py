@@ -63,6 +63,7 @@ def test_methods_on_ragged_and_edge_budgets(method):
     check(method, tok, 3, 16 * 300, 16, 37, 40, seed=3)
     check(method, tok, 3, 16 * 300, 16, 300, 40, seed=3)          # k == C: everything
     check(method, tok, 3, 16 * 300, 16, 1000, 40, seed=3)         # k > C
+    check(method, tok, 3, 16 * 300, 16, 0, 40, seed=3)            # k == 0: the status word is still cleared
     check(method, np.zeros(4 * 256, np.int32), 4, 256, 32, 3, 8, seed=5)   # all ties
 
 
