@@ -2,7 +2,8 @@
 workspace form (pulsar_phase2_query) through the C ABI: the same inputs give
 bit-identical partial outputs and log-sum-exps, on two calls in a row, the
 second on a smaller problem (the fixed array keeps the first call's contents),
-and the merged result of the no-allocation call is checked against the oracle."""
+and the merged result of the no-allocation call is checked against the oracle.
+The entry point also replays from a HIP graph."""
 import numpy as np
 import pytest
 
@@ -84,3 +85,42 @@ def test_noalloc_query_equals_the_workspace_query():
             assert_close(o[s].cpu().numpy(), want_o, f"noalloc call {j} merged O seq {s}")
             assert_close(lse[s].cpu().numpy(), want_lse, f"noalloc call {j} merged LSE seq {s}",
                          max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+def test_noalloc_query_replays_from_a_graph():
+    """The callers the entry point is for capture it: a HIP graph of one call,
+    replayed three times over poisoned outputs, with an eager no-allocation call of
+    another shape between replays (it overwrites the fixed array), equals the eager
+    call bit for bit every time."""
+    torch = torch_cuda()
+    from long_context_blockwise_max_amd import binding as B
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+        torch.bfloat16).to("cuda")
+    shape, other = CALLS[1], CALLS[0]
+    batch, n_shards, shard_len, q_len, hq, hkv, d, with_self = shape
+    tensors = tuple(dev(x) for x in _inputs(batch, n_shards, shard_len, q_len, hq, hkv, d, seed=77))
+    attn = B.make_attn(hq, hkv, d, 500000.0, 0)
+    o_want, l_want, n_parts = _run(True, attn, shape, tensors)
+    o_part = torch.empty_like(o_want)
+    lse_part = torch.empty_like(l_want)
+    qq, kc, vc, ks, vs = tensors
+    args = (attn, batch, n_shards, shard_len, qq, q_len, n_shards * shard_len, kc, vc, ks, vs,
+            o_part, lse_part, n_parts)
+    ob = other
+    other_tensors = tuple(dev(x) for x in _inputs(*ob[:7], seed=78))
+    other_attn = B.make_attn(ob[4], ob[5], ob[6], 500000.0, 0)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        B.pulsar_phase2_query_noalloc(*args)
+    for rep in range(3):
+        o_part.fill_(float("nan"))
+        lse_part.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.nan_to_num(o_part, nan=7.0), torch.nan_to_num(o_want, nan=7.0)), rep
+        assert torch.equal(lse_part, l_want), rep
+        log(f"[noalloc] graph replay {rep}: bit-identical to the eager call")
+        _run(True, other_attn, ob, other_tensors)    # another shape through the same array
